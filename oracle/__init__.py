@@ -1,0 +1,110 @@
+"""Oracle for the attention forward pass (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The HIP path
+never imports it and shares no code with it.
+
+Two functions:
+
+* :func:`attention_rows` / :func:`attention` -- the explicit definition of
+  softmax attention in fp64 (C, ``attention_ref.c``): S = scale*QK^T,
+  P = softmax(S), O = PV and LSE = log sum exp(S) per row ("A09 - Advanced
+  Triton & FlashAttention", section 2; "Building a Verifiable FlashAttention
+  Forward from PyTorch to Triton", Part 1).
+* :func:`oracle.tiled.tiled_attention` -- the online-softmax tile recurrence
+  in fp64 (numpy), used to check that the recurrence reaches the explicit
+  result.
+
+Pins that tie these to the pages and to mathematics (not to themselves) live
+in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attention_ref.c")
+LIBRARY = os.path.join(_HERE, "liboracle_attention.so")
+
+# -ffp-contract=off: every product and sum is rounded on its own, as written.
+GCC_FLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the C oracle with gcc (no GPU involved)."""
+    cmd = ["gcc", *GCC_FLAGS, "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+_lib_cache: dict = {}
+
+
+def load(path: str = LIBRARY):
+    """Load (building if absent or stale) the oracle library at ``path``."""
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if path == LIBRARY and (not os.path.exists(path)
+                            or os.path.getmtime(path) < os.path.getmtime(SOURCE)):
+        build()
+    lib = ctypes.CDLL(path)
+    fn = lib.oracle_attention_rows
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 4 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p]
+    _lib_cache[path] = lib
+    return lib
+
+
+def _as_bhnd(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 3:
+        return x
+    if x.ndim == 4:
+        return x.reshape(x.shape[0] * x.shape[1], x.shape[2], x.shape[3])
+    raise ValueError("expected [BH, N, D] or [B, H, N, D]")
+
+
+def attention_rows(q, k, v, scale, causal, rows, n_kv=None, lib_path=LIBRARY):
+    """O and LSE for the listed rows.
+
+    q, k, v: float32 arrays [B, H, N, D] or [BH, N, D] holding exact input
+    values. rows: int array of shape [R, 2] with (flattened head bh, query i).
+    n_kv: keys >= n_kv are masked (default N). Returns (o [R, D], lse [R]) fp64.
+    """
+    q3, k3, v3 = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v)
+    BH, N, D = q3.shape
+    if k3.shape != q3.shape or v3.shape != q3.shape:
+        raise ValueError("q, k, v must have the same shape")
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    R = rows.shape[0]
+    o = np.empty((R, D), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    if n_kv is None:
+        n_kv = N
+    rc = load(lib_path).oracle_attention_rows(
+        q3.ctypes.data, k3.ctypes.data, v3.ctypes.data, BH, N, int(n_kv), D,
+        float(scale), int(bool(causal)), rows.ctypes.data, R,
+        o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attention_rows failed with code {rc}")
+    return o, lse
+
+
+def attention(q, k, v, scale, causal, n_kv=None, lib_path=LIBRARY):
+    """O [..., N, D] and LSE [..., N] for every row (small inputs only)."""
+    q = np.asarray(q)
+    lead = q.shape[:-2]
+    N, D = q.shape[-2:]
+    BH = int(np.prod(lead)) if lead else 1
+    bh, i = np.meshgrid(np.arange(BH), np.arange(N), indexing="ij")
+    rows = np.stack([bh.ravel(), i.ravel()], axis=1)
+    o, lse = attention_rows(q.reshape(BH, N, D), np.asarray(k).reshape(BH, N, D),
+                            np.asarray(v).reshape(BH, N, D), scale, causal, rows,
+                            n_kv, lib_path)
+    return o.reshape(*lead, N, D), lse.reshape(*lead, N)
