@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 FlashAttention-2 forward (one GPU).
+
+A step is one fa_fwd call over the whole batch of the headline workload,
+[B=4, H=16, N=4096, D=128] bf16, non-causal, inputs resident in HBM. Prints
+one JSON line: attention TFLOP/s (4*B*H*N^2*D FLOPs, halved for causal, the
+count of "FlashAttention 2 from PyTorch to Triton", Step 4), the fraction of
+the MI355X dense bf16 MFMA peak, the same figures for the causal mask and the
+other N=4096 workload in "extra", and the fp64 CPU oracle timed on a bounded
+sample of the same workload as "cpu_baseline".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fa_inputs  # noqa: E402
+
+# MI355X published dense MFMA peak for bf16/fp16 (256 CUs x 4096 FLOP/clk x 2.4 GHz)
+PEAK_BF16_TFLOPS = 2516.6
+METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak at N=4096 (causal/non-causal)"
+
+
+def attention_flops(B, H, N, D, causal):
+    """4*B*H*N^2*D, halved for causal (two N x N x D matmuls, 2 FLOPs per MAC)."""
+    f = 4 * B * H * N * N * D
+    return f / 2 if causal else f
+
+
+def attention_bytes(B, H, N, D, esize, with_lse=True):
+    """Algorithmic HBM bytes: Q, K, V read once and O written once, plus the
+    fp32 LSE ("A09 - Advanced Triton & FlashAttention", section 2: fused
+    traffic per head is 4*N*d elements)."""
+    return 4 * B * H * N * D * esize + (4 * B * H * N if with_lse else 0)
+
+
+def _device_inputs(w, torch):
+    qb, kb, vb = fa_inputs.workload_inputs(w)
+    dt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def dev(b):
+        t = torch.from_numpy(b)
+        if w.dtype != "fp32":
+            t = t.view(torch.int16).view(dt)
+        return t.cuda()
+    return (dev(qb), dev(kb), dev(vb)), (qb, kb, vb)
+
+
+def time_gpu(w, causal, steps, warmup, torch, fa):
+    """Median-free whole-run timing: `warmup` untimed calls, then `steps` calls
+    bracketed by synchronisation and events on the launch stream."""
+    (q, k, v), _ = _device_inputs(w, torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    flops = attention_flops(w.B, w.H, w.N, w.D, causal)
+    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,
+            "flops": flops}
+
+
+def cpu_baseline(w, causal, target_s=12.0):
+    """The fp64 oracle on a bounded sample of rows of the same workload."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    qb, kb, vb = fa_inputs.workload_inputs(w)
+    q, k, v = (fa_inputs.to_f32(x, w.dtype) for x in (qb, kb, vb))
+    rng = np.random.default_rng(123)
+    BH = w.B * w.H
+
+    def run(n_rows):
+        rows = np.stack([rng.integers(0, BH, n_rows), rng.integers(0, w.N, n_rows)], 1)
+        flops = sum(4 * ((i + 1) if causal else w.N) * w.D for i in rows[:, 1])
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, w.scale, causal, rows)
+        return time.perf_counter() - t0, flops
+
+    probe_rows = 64
+    t, f = run(probe_rows)
+    n_rows = int(min(1 << 20, max(probe_rows, probe_rows * target_s / max(t, 1e-3))))
+    t, f = run(n_rows)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
+            "kind": "oracle",
+            "sample": f"{n_rows} random query rows of {w.name} ({'causal' if causal else 'non-causal'}),"
+                      f" explicit fp64 attention per row, {t:.1f} s, {f / 1e9:.1f} GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=fa_inputs.HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the attention "
+              "forward shards over (batch, head) with no communication, so the "
+              "per-GPU figure is the one that matters; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_10_amd as fa
+    fa.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = fa_inputs.WORKLOADS[a.workload]
+    head = time_gpu(w, False, a.steps, a.warmup, torch, fa)
+    print(f"[bench] {w.name} non-causal: {head['ms']:.4f} ms/step {head['tflops']:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    extra = {}
+    if not a.no_extra:
+        for name, causal in ((w.name, True), ("b4h16_n4096_d64_bf16", False),
+                             ("b4h16_n4096_d64_bf16", True)):
+            r = time_gpu(fa_inputs.WORKLOADS[name], causal, max(10, a.steps // 2),
+                         max(5, a.warmup // 2), torch, fa)
+            key = f"{name}_{'causal' if causal else 'noncausal'}"
+            extra[key] = {"ms": round(r["ms"], 5), "tflops": round(r["tflops"], 2),
+                          "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
+            print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+
+    esize = fa_inputs.ESIZE[w.dtype]
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(head["tflops"], 3),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "algorithmic_flops_per_launch": head["flops"],
+        "algorithmic_bytes_per_launch": attention_bytes(w.B, w.H, w.N, w.D, esize),
+        "kernel": "fa_fwd_kernel<bf16, D=128, non-causal>",
+    }
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(w, False)
+        print(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "dtype": w.dtype, "causal": False, "scale": w.scale,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+"""Python binding of the gfx950 FlashAttention-2 forward library.
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels of ``libfa_mi355x.so`` (built by ``exact_attention_10_amd.build``).
+PyTorch supplies device memory and streams. There is no fallback: if the
+library is missing, calls raise ``RuntimeError``.
+
+The functions mirror the C ABI of ``include/fa.h``:
+
+* :func:`fa_fwd` -- O = softmax(scale * Q K^T) V and the row log-sum-exp;
+* :func:`fa_fwd_nk` -- the same with only the first ``n_kv`` keys visible;
+* :func:`fa_fwd_variant` -- run a named kernel variant (tuning);
+* :func:`fa_num_variants`, :func:`fa_variant_name`, :func:`fa_strerror`,
+  :func:`fa_version`.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libfa_mi355x.so")
+
+FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGNMENT, FA_ERR_HIP = 0, -1, -2, -3, -4
+
+# names and argument types of every exported symbol of include/fa.h
+_P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
+    "fa_fwd_nk": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
+    "fa_fwd_variant": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P, _I]),
+    "fa_num_variants": (_I, []),
+    "fa_variant_name": (ctypes.c_char_p, [_I]),
+    "fa_strerror": (ctypes.c_char_p, [_I]),
+    "fa_version": (_I, []),
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+def load_library(path: str = LIBRARY):
+    """Load the HIP library; raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_attention_10_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_DTYPE_FP32, torch.float16: FA_DTYPE_FP16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check(code: int):
+    if code != FA_OK:
+        raise FAError(code, fa_strerror(code))
+
+
+def _prepare(q, k, v, o, lse, with_lse):
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous tensor like q")
+    if lse is None and with_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != q.shape[:3] or lse.dtype != torch.float32
+                              or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    return o, lse
+
+
+def _stream_handle(q, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fa_fwd_variant(q, k, v, o=None, lse=None, *, n_kv=None, causal=False, scale=None,
+                   stream=None, variant=0, with_lse=True):
+    """Run kernel variant ``variant``; returns (o, lse). See include/fa.h."""
+    lib = load_library()
+    o, lse = _prepare(q, k, v, o, lse, with_lse)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    n_kv = N if n_kv is None else int(n_kv)
+    rc = lib.fa_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr() if lse is not None else None,
+                            B, H, N, n_kv, D, int(bool(causal)), float(scale),
+                            _dtype_code(q), _stream_handle(q, stream), int(variant))
+    _check(rc)
+    return o, lse
+
+
+def fa_fwd_nk(q, k, v, o=None, lse=None, *, n_kv, causal=False, scale=None, stream=None,
+              with_lse=True):
+    """Attention with only the first ``n_kv`` keys visible; returns (o, lse)."""
+    lib = load_library()
+    o, lse = _prepare(q, k, v, o, lse, with_lse)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = lib.fa_fwd_nk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr() if lse is not None else None,
+                       B, H, N, int(n_kv), D, int(bool(causal)), float(scale),
+                       _dtype_code(q), _stream_handle(q, stream))
+    _check(rc)
+    return o, lse
+
+
+def fa_fwd(q, k, v, o=None, lse=None, *, causal=False, scale=None, stream=None,
+           with_lse=True):
+    """O = softmax(scale * Q K^T) V over [B, H, N, D] tensors; returns (o, lse).
+
+    ``scale`` defaults to 1/sqrt(D). ``lse`` is fp32 [B, H, N] (natural log) or
+    None when ``with_lse`` is False. Asynchronous on ``stream`` (default: the
+    current torch stream).
+    """
+    lib = load_library()
+    o, lse = _prepare(q, k, v, o, lse, with_lse)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                    lse.data_ptr() if lse is not None else None,
+                    B, H, N, D, int(bool(causal)), float(scale), _dtype_code(q),
+                    _stream_handle(q, stream))
+    _check(rc)
+    return o, lse
+
+
+def fa_num_variants() -> int:
+    return load_library().fa_num_variants()
+
+
+def fa_variant_name(variant: int) -> str:
+    return load_library().fa_variant_name(int(variant)).decode()
+
+
+def fa_strerror(code: int) -> str:
+    return load_library().fa_strerror(int(code)).decode()
+
+
+def fa_version() -> int:
+    return load_library().fa_version()

@@ -1,0 +1,207 @@
+// Host side of the gfx950 FlashAttention-2 forward library: argument
+// validation, kernel selection and launch behind the C ABI of include/fa.h.
+//
+// Every argument is validated before the first HIP call, so the library can
+// be loaded and its error paths exercised on a machine without a GPU. The
+// library allocates no memory and keeps no state; a launch is asynchronous on
+// the caller's stream.
+#include "fa.h"
+#include "fa_kernel.hpp"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+struct Variant {
+  const char *name;
+  int xcd_remap;
+};
+
+// Variants of the same kernel family; 0 is what fa_fwd runs.
+const Variant kVariants[] = {
+    {"bm128_bn64_xcd", 1},
+    {"bm128_bn64_linear", 0},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+using KernelFn = void (*)(fa::Params);
+
+template <int DT, int D, bool CAUSAL>
+struct Inst {
+  static const void *fn() { return reinterpret_cast<const void *>(&fa::fa_fwd_kernel<DT, D, CAUSAL>); }
+  static constexpr int lds = fa::Cfg<DT, D, CAUSAL>::LDS_BYTES;
+  static constexpr int bm = fa::Cfg<DT, D, CAUSAL>::BM;
+};
+
+struct Launch {
+  const void *fn;
+  int lds;
+  int bm;
+};
+
+template <int DT, int D>
+Launch pick_causal(int causal) {
+  if (causal) return {Inst<DT, D, true>::fn(), Inst<DT, D, true>::lds, Inst<DT, D, true>::bm};
+  return {Inst<DT, D, false>::fn(), Inst<DT, D, false>::lds, Inst<DT, D, false>::bm};
+}
+
+bool pick(int dtype, int64_t D, int causal, Launch *out) {
+  switch (dtype) {
+    case FA_DTYPE_BF16:
+      if (D == 64) { *out = pick_causal<fa::DT_BF16, 64>(causal); return true; }
+      if (D == 128) { *out = pick_causal<fa::DT_BF16, 128>(causal); return true; }
+      return false;
+    case FA_DTYPE_FP16:
+      if (D == 64) { *out = pick_causal<fa::DT_FP16, 64>(causal); return true; }
+      if (D == 128) { *out = pick_causal<fa::DT_FP16, 128>(causal); return true; }
+      return false;
+    case FA_DTYPE_FP32:
+      if (D == 64) { *out = pick_causal<fa::DT_FP32, 64>(causal); return true; }
+      if (D == 128) { *out = pick_causal<fa::DT_FP32, 128>(causal); return true; }
+      return false;
+    default:
+      return false;
+  }
+}
+
+int elem_bytes(int dtype) {
+  return dtype == FA_DTYPE_FP32 ? 4 : (dtype == FA_DTYPE_FP16 || dtype == FA_DTYPE_BF16) ? 2 : 0;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
+}
+
+int validate(const void *q, const void *k, const void *v, void *o, float *lse,
+             int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D,
+             float scale, int dtype) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (n_kv < 0 || n_kv > N) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  const int es = elem_bytes(dtype);
+  if (es == 0) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  // one head must be addressable with 32-bit byte offsets
+  if (N > (INT64_C(0x7fffffff) / (D * es))) return FA_ERR_UNSUPPORTED;
+  const int64_t tiles = (N + 127) / 128;
+  if (B > INT64_C(0x7fffffff) / H || B * H > INT64_C(0x7fffffff) / tiles) return FA_ERR_UNSUPPORTED;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                        reinterpret_cast<uintptr_t>(lse);
+  if (mis & 15) return FA_ERR_ALIGNMENT;
+  const int64_t tbytes = B * H * N * D * es;  // < 2^62 given the limits above
+  const void *ins[3] = {q, k, v};
+  for (const void *x : ins)
+    if (overlaps(o, tbytes, x, tbytes)) return FA_ERR_INVALID_ARG;
+  if (lse) {
+    const int64_t lbytes = B * H * N * (int64_t)sizeof(float);
+    for (const void *x : ins)
+      if (overlaps(lse, lbytes, x, tbytes)) return FA_ERR_INVALID_ARG;
+    if (overlaps(lse, lbytes, o, tbytes)) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+int launch(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D, int causal,
+           float scale, int dtype, void *stream, int variant) {
+  int rc = validate(q, k, v, o, lse, B, H, N, n_kv, D, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
+  Launch L;
+  if (!pick(dtype, D, causal, &L)) return FA_ERR_UNSUPPORTED;
+
+  fa::Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.N = N;
+  p.n_kv = n_kv;
+  p.nq_tiles = (int)((N + L.bm - 1) / L.bm);
+  p.xcd_remap = kVariants[variant].xcd_remap;
+  // scale * log2(e), formed in double and rounded once
+  p.c = (float)((double)scale * 1.4426950408889634);
+
+  const dim3 grid((unsigned)(B * H * p.nq_tiles));
+  const dim3 block(256);
+  void *args[] = {&p};
+  hipError_t e = hipLaunchKernel(L.fn, grid, block, args, (size_t)L.lds,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_error, sizeof(g_hip_error), "%s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+// Kernels that use more than 64 KB of LDS must opt in once per process.
+struct LdsOptIn {
+  static void apply() {
+    static std::once_flag once;
+    std::call_once(once, [] {
+    (void)hipFuncSetAttribute(Inst<fa::DT_FP32, 128, false>::fn(),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Inst<fa::DT_FP32, 128, false>::lds);
+    (void)hipFuncSetAttribute(Inst<fa::DT_FP32, 128, true>::fn(),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Inst<fa::DT_FP32, 128, true>::lds);
+    });
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D,
+                   int causal, float scale, int dtype, void *stream, int variant) {
+  int rc = validate(q, k, v, o, lse, B, H, N, n_kv, D, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_DTYPE_FP32 && D == 128) LdsOptIn::apply();
+  return launch(q, k, v, o, lse, B, H, N, n_kv, D, causal, scale, dtype, stream, variant);
+}
+
+int fa_fwd_nk(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D, int causal,
+              float scale, int dtype, void *stream) {
+  return fa_fwd_variant(q, k, v, o, lse, B, H, N, n_kv, D, causal, scale, dtype, stream, 0);
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+           int dtype, void *stream) {
+  return fa_fwd_variant(q, k, v, o, lse, B, H, N, N, D, causal, scale, dtype, stream, 0);
+}
+
+int fa_num_variants(void) { return kNumVariants; }
+
+const char *fa_variant_name(int variant) {
+  return (variant >= 0 && variant < kNumVariants) ? kVariants[variant].name : "";
+}
+
+const char *fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, variant or size";
+    case FA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case FA_ERR_HIP: return g_hip_error;
+    default: return "unknown status code";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,407 @@
+// FlashAttention-2 forward kernel for gfx950 (CDNA4), hand-written HIP.
+//
+// One workgroup owns one (batch*head, query tile) pair: 4 waves, 32 query rows
+// per wave, 128 rows per tile. The workgroup streams the head's key/value tiles
+// (64 keys each) through LDS, double-buffered, with direct global->LDS buffer
+// loads; each wave keeps the online-softmax state of its 32 rows in registers
+// and never writes a score to memory ("A09 - Advanced Triton &
+// FlashAttention", section 3, The kernel, in pseudocode; "Triton:
+// FlashAttention-2 Forward Pass", Decomposition).
+//
+// Matrix products run on MFMA with fp32 accumulation. Scores are computed
+// transposed, S^T = K Q^T, so that a lane owns one query column of the 32x32
+// accumulator: row max and row sum are in-lane plus one swap between the two
+// 32-lane halves, and the per-row rescale factor is a per-lane scalar. The
+// output is accumulated transposed as well, O^T += V^T P^T, so P goes from the
+// score accumulator to the MFMA B operand without leaving registers; the key
+// order that the accumulator layout imposes on P is applied to V when it is
+// read from LDS with the transposing LDS read.
+//
+// Online softmax ("A09", section 3, The rescaling update, written out;
+// "Building a Verifiable FlashAttention Forward from PyTorch to Triton",
+// Part 3 Step 4): with c = scale*log2(e), the running max m is kept in base-2
+// units, p = exp2(s*c - m) is one FMA and one exp, alpha = exp2(m_old - m_new)
+// rescales l and the accumulator, and O = acc / l once at the end. LSE is
+// (m + log2 l) * ln 2. A row that has seen no visible key keeps m = -inf; the
+// exponent reference is then taken as 0 so no NaN can arise, and such a row
+// ends with O = 0, LSE = -inf ("Triton: FlashAttention-2 Forward Pass", The
+// rescale direction).
+//
+// Causal attention (top-left) stops the key loop after the tile's last query
+// row and applies the element mask only on tiles that straddle the diagonal
+// or the end of the keys ("A09", section 3, Causal masking: skipping beats
+// masking; "How to profile and optimise kernels", Round 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+enum { DT_FP32 = 0, DT_FP16 = 1, DT_BF16 = 2 };
+
+struct Params {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;          // may be null
+  int64_t N;           // rows per head (query and key length)
+  int64_t n_kv;        // keys j >= n_kv are masked (n_kv <= N)
+  int nq_tiles;        // ceil(N / BM)
+  int xcd_remap;       // 1: map workgroups so that one XCD works on few heads
+  float c;             // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// Element traits. 16-bit types use the 32x32x16 MFMA (8 elements per lane per
+// operand); fp32 uses the 32x32x2 MFMA (1 element per lane per operand).
+
+template <int DT> struct Elem;
+template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; static constexpr int k_step = 16; };
+template <> struct Elem<DT_FP16> { static constexpr int bytes = 2; static constexpr int k_step = 16; };
+template <> struct Elem<DT_FP32> { static constexpr int bytes = 4; static constexpr int k_step = 2; };
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  // Raw buffer resource: base address, stride 0, num_records = bytes, gfx9
+  // data-format word. Reads at byte offsets >= bytes return 0.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// vmcnt(0): wait until this wave's outstanding vector-memory operations,
+// including LDS-direct loads, have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Max over the two 32-lane halves: both halves end with the same value.
+__device__ __forceinline__ float halves_max(float x) {
+  u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
+      __float_as_uint(x), __float_as_uint(x), false, false));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
+      __float_as_uint(x), __float_as_uint(x), false, false));
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS row swizzle: the 16-byte chunk c of tile row r is stored at chunk
+// c ^ swz(r). Chosen so that (a) 16 consecutive rows read at the same chunk
+// (K operand reads) fall in 16 different chunks, and (b) the 4-row x 64-byte
+// blocks of the transposing V reads of one half-wave cover all 64 banks.
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (ROW_BYTES >= 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+
+template <int DT, int D, bool CAUSAL>
+struct Cfg {
+  static constexpr int WAVES = 4;
+  static constexpr int BM = WAVES * 32;     // query rows per workgroup
+  static constexpr int BN = 64;             // keys per tile
+  static constexpr int ES = Elem<DT>::bytes;
+  static constexpr int ROW_BYTES = D * ES;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;            // one K or V tile
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;             // K,V x 2 buffers
+  static constexpr int LOADS_PER_THREAD = TILE_BYTES / (WAVES * 64 * 16);
+  static_assert(TILE_BYTES % (WAVES * 64 * 16) == 0, "tile must split into 16-byte lane loads");
+};
+
+// Register budget: two waves per SIMD (256 VGPRs) for 16-bit inputs, one wave
+// per SIMD for fp32, whose Q fragments are twice as wide.
+template <int DT, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Params p) {
+  using C = Cfg<DT, D, CAUSAL>;
+  constexpr int ES = C::ES, BN = C::BN, BM = C::BM, RB = C::ROW_BYTES;
+  constexpr int KSTEP = Elem<DT>::k_step;
+  constexpr int NKC = D / KSTEP;           // MFMAs along the head dim for S^T
+  constexpr int NKB = BN / 32;             // 32-key blocks per tile
+  constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O^T
+  constexpr int NPC = BN / KSTEP;          // MFMAs along the keys for O^T
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- which (head, query tile) this workgroup owns ----
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if (p.xcd_remap && (nblk & 7) == 0) {
+    // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+    // contiguous range of (head, tile) pairs so the tiles of one head share
+    // that XCD's L2.
+    bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  }
+  const int bh = bid / p.nq_tiles;
+  int qt = bid - bh * p.nq_tiles;
+  if (CAUSAL) qt = p.nq_tiles - 1 - qt;    // longest causal tiles first
+  const int64_t N = p.N;
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * 32;           // first query row of this wave
+  const int my_q = qw + l32;               // the query row this lane owns
+
+  const int64_t head_elems = N * (int64_t)D;
+  const char *qh = (const char *)p.q + (int64_t)bh * head_elems * ES;
+  const char *kh = (const char *)p.k + (int64_t)bh * head_elems * ES;
+  const char *vh = (const char *)p.v + (int64_t)bh * head_elems * ES;
+
+  const int n_kv = (int)p.n_kv;
+  int kend = n_kv;
+  if (CAUSAL) kend = min(kend, q0 + BM);
+  const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), straight from global ----
+  // lane (q = l32, half) holds Q[my_q][kc*KSTEP + half*KSTEP/2 ...]
+  constexpr int QE = KSTEP / 2;             // elements per lane per fragment
+  typedef uint16_t qraw_t __attribute__((ext_vector_type(8)));
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(head_elems * ES));
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kh, (uint32_t)((int64_t)n_kv * D * ES));
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vh, (uint32_t)((int64_t)n_kv * D * ES));
+
+  // fragments stored as raw 32-bit words
+  constexpr int QW = (QE * ES) / 4;          // 32-bit words per Q fragment
+  uint32_t qf[NKC][QW];
+  {
+    const uint32_t row_off = (uint32_t)my_q * RB;
+    const bool row_ok = my_q < N;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const uint32_t off = row_off + (uint32_t)((kc * KSTEP + half * QE) * ES);
+      if constexpr (QW == 4) {
+        u32x4 x = row_ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off, 0, 0))
+                         : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qf[kc][w] = x[w];
+      } else {
+        qf[kc][0] = row_ok ? __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, off, 0, 0) : 0u;
+      }
+    }
+  }
+
+  // ---- K/V tile staging: direct global->LDS loads into a swizzled layout ----
+  auto issue_tile = [&](int t, int buf) {
+    const int kstart = t * BN;
+    char *kl = smem + buf * (2 * C::TILE_BYTES);
+    char *vl = kl + C::TILE_BYTES;
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_THREAD; ++u) {
+      const int inst = wave * C::LOADS_PER_THREAD + u;          // 1 KB of LDS each
+      const int lds_off = inst * 1024 + lane * 16;
+      const int row = lds_off / RB;
+      const int pchunk = (lds_off % RB) / 16;
+      const int lchunk = pchunk ^ swz<RB>(row);
+      const uint32_t goff = (uint32_t)(kstart + row) * RB + lchunk * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (FA_LDS void *)(kl + inst * 1024), 16, goff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (FA_LDS void *)(vl + inst * 1024), 16, goff, 0, 0, 0);
+    }
+  };
+
+  // ---- running state ----
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY;     // running max (base-2 units), same in both halves
+  float l_run = 0.f;           // this lane's partial row sum (its half's keys)
+  const float c = p.c;
+
+  if (n_tiles > 0) issue_tile(0, 0);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    wait_vmem();
+    __syncthreads();                        // tile t visible; buffer (t+1)&1 free
+    if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+
+    const int kstart = t * BN;
+    if (CAUSAL && kstart > qw + 31) continue;   // every key of this tile is in this wave's future
+
+    const char *kl = smem + (t & 1) * (2 * C::TILE_BYTES);
+    const char *vl = kl + C::TILE_BYTES;
+
+    // ---- S^T = K Q^T : NKB blocks of 32 keys x 32 queries ----
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      const int row = kb * 32 + l32;
+      const char *rowp = kl + row * RB;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        if constexpr (DT == DT_FP32) {
+          const int col = kc * 2 + half;                       // element
+          const int ch = (col / 4) ^ swz<RB>(row);
+          const float a = *(const FA_LDS float *)(rowp + ch * 16 + (col % 4) * 4);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, __uint_as_float(qf[kc][0]), s[kb], 0, 0, 0);
+        } else {
+          const int ch = (kc * 2 + half) ^ swz<RB>(row);
+          const u32x4 a = *(const FA_LDS u32x4 *)(rowp + ch * 16);
+          u32x4 b = {qf[kc][0], qf[kc][1], qf[kc][2], qf[kc][3]};
+          if constexpr (DT == DT_BF16)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), s[kb], 0, 0, 0);
+          else
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), s[kb], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- masks: only on tiles past the end of the keys or on the diagonal ----
+    const bool need_mask = (kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kstart + kb * 32 + 8 * (i / 4) + half * 4 + (i % 4);
+          const bool bad = (key >= n_kv) || (CAUSAL && key > my_q);
+          if (bad) s[kb][i] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax ----
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    const float neg = -m_ref;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, neg));
+        s[kb][i] = e;
+        rs += e;
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    // alpha is exactly 1 when the max did not move; skip the rescale when that
+    // holds for every lane of the wave (the product would be unchanged).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T ----
+    if constexpr (DT == DT_FP32) {
+#pragma unroll
+      for (int pc = 0; pc < NPC; ++pc) {
+        const int kb = pc / 16, i = pc % 16;
+        const int key = kb * 32 + 8 * (i / 4) + half * 4 + (i % 4);   // tile-local
+        const float pv = s[kb][i];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int col = db * 32 + l32;
+          const int ch = (col / 4) ^ swz<RB>(key);
+          const float a = *(const FA_LDS float *)(vl + key * RB + ch * 16 + (col % 4) * 4);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pv, acc[db], 0, 0, 0);
+        }
+      }
+    } else {
+      // P^T chunk pc = 16 keys: this lane's values i = (pc%2)*8 .. +7 of block pc/2,
+      // i.e. keys pc*16 + 8*(j/4) + half*4 + (j%4), j = 0..7, rounded to the input type.
+#pragma unroll
+      for (int pc = 0; pc < NPC; ++pc) {
+        const int kb = pc / 2, i0 = (pc % 2) * 8;
+        u32x4 b;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = s[kb][i0 + 2 * w], x1 = s[kb][i0 + 2 * w + 1];
+          if constexpr (DT == DT_BF16) {
+            __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+            b[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          } else {
+            _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+            b[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          }
+        }
+        // V^T operand for lane (d = db*32 + l32, half): V[k0 + 0..3][d] and
+        // V[k0 + 8 + 0..3][d], k0 = pc*16 + half*4, via the transposing read:
+        // within each 16-lane group, lane g16 = 4*r + cq addresses row k + r,
+        // head-dim columns 4*cq .. 4*cq+3 of the group's 16 columns.
+        const int g = lane >> 4, g16 = lane & 15;
+        const int r = g16 >> 2, cq = g16 & 3;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int col = db * 32 + (g & 1) * 16 + cq * 4;        // element column
+          u32x4 a;
+#pragma unroll
+          for (int jg = 0; jg < 2; ++jg) {
+            const int key = pc * 16 + jg * 8 + (g >> 1) * 4 + r;
+            const int ch = ((col * 2) / 16) ^ swz<RB>(key);
+            const char *addr = vl + key * RB + ch * 16 + (col * 2) % 16;
+            s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)addr);
+            u32x2 xx = __builtin_bit_cast(u32x2, x);
+            a[jg * 2] = xx[0];
+            a[jg * 2 + 1] = xx[1];
+          }
+          if constexpr (DT == DT_BF16)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[db], 0, 0, 0);
+          else
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- finalize: O = acc / l, LSE = (m + log2 l) ln 2 ----
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (my_q < N) {
+    char *orow = (char *)p.o + ((int64_t)bh * head_elems + (int64_t)my_q * D) * ES;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = db * 32 + 8 * gq + half * 4;
+        if constexpr (DT == DT_FP32) {
+          float4 w = {acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv,
+                      acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
+          *(float4 *)(orow + d0 * 4) = w;
+        } else {
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float x0 = acc[db][gq * 4 + 2 * h] * inv, x1 = acc[db][gq * 4 + 2 * h + 1] * inv;
+            if constexpr (DT == DT_BF16) {
+              __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+              w[h] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            } else {
+              _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+              w[h] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            }
+          }
+          *(u32x2 *)(orow + d0 * 2) = u32x2{w[0], w[1]};
+        }
+      }
+    if (p.lse && half == 0) {
+      const float lse = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+      p.lse[(int64_t)bh * N + my_q] = lse;
+    }
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,108 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library.
+ *
+ * The operation: exact scaled-dot-product attention O = softmax(scale*Q K^T) V
+ * per (batch, head), computed tile by tile with the online softmax (running
+ * row max m, running denominator l, unnormalised fp32 accumulator; both l and
+ * the accumulator rescaled by exp(m_old - m_new) on every key tile, a single
+ * division at the end), so the N x N score matrix never exists in memory.
+ * Defined on "A09 - Advanced Triton & FlashAttention" (section 3, The
+ * rescaling update, written out, and The kernel, in pseudocode) and
+ * "FlashAttention 2 from PyTorch to Triton" (What I am building: the FA2
+ * forward and its row log-sum-exp output L = m + log l). The tensor contract
+ * (contiguous [B, H, N, D], fp16/bf16, causal or not, head dim 64 or 128)
+ * follows the scope of "Building a Verifiable FlashAttention Forward from
+ * PyTorch to Triton"; an fp32 path is added as a precision check.
+ *
+ * Conventions shared by every entry point:
+ *  - q, k, v, o are device pointers to contiguous row-major [B, H, N, D]
+ *    tensors of element type `dtype`; o has the same type as the inputs.
+ *  - lse is a device pointer to a contiguous fp32 [B, H, N] tensor, or NULL
+ *    (then the log-sum-exp is not written). LSE uses the natural log.
+ *  - causal != 0 applies the top-left causal mask: query i sees key j only
+ *    when j <= i ("Building a Verifiable FlashAttention Forward", Part 1).
+ *  - scale multiplies Q K^T; it must be finite and > 0 (the usual value is
+ *    1/sqrt(D)).
+ *  - Ownership: the caller owns every buffer; the library allocates no device
+ *    memory and keeps no state between calls.
+ *  - The call is asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *    NULL = the null stream). It returns after the kernel is enqueued; the
+ *    outputs are valid once the caller has synchronised that stream. A fault
+ *    on the device is reported by that synchronisation, not by the return.
+ *  - o and lse must not overlap q, k, v or each other (checked on the host).
+ *  - Error behaviour: every argument is validated before any HIP call. On an
+ *    invalid argument nothing is launched and a negative code is returned;
+ *    the outputs are left untouched. Thread-safe and reentrant.
+ *  - Limits: 1 <= B, H, N; B*H*ceil(N/128) < 2^31 workgroups; one head's
+ *    tensor (N*D*element size bytes) must be below 2^31 bytes; pointers must
+ *    be 16-byte aligned.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype { FA_DTYPE_FP32 = 0, FA_DTYPE_FP16 = 1, FA_DTYPE_BF16 = 2 };
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, bad scale, overlap   */
+  FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, unknown dtype, too large */
+  FA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned              */
+  FA_ERR_HIP = -4          /* the HIP launch failed; see fa_strerror        */
+};
+
+/*
+ * Attention forward for self-attention of length N: O [B,H,N,D] and, when
+ * lse != NULL, LSE [B,H,N] = m + log(l) per row (natural log, fp32).
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+           int dtype, void *stream);
+
+/*
+ * As fa_fwd, with only the first n_kv keys (0 <= n_kv <= N) visible: keys
+ * j >= n_kv are masked for every query. The query and key lengths play
+ * separate roles, as "Triton: FlashAttention-2 Forward Pass" (Masks and
+ * sentinels) asks. With n_kv = 0 every row sees no key; such a row gets
+ * O = 0 and LSE = -inf (the guard for fully masked rows of that page's
+ * "The rescale direction"). fa_fwd(...) equals fa_fwd_nk(..., N, ...).
+ */
+int fa_fwd_nk(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D,
+              int causal, float scale, int dtype, void *stream);
+
+/*
+ * Tuning entry: as fa_fwd_nk but runs kernel variant `variant` (0 = the
+ * default choice of fa_fwd; 1 .. fa_num_variants()-1 = alternative tile
+ * shapes / schedules of the same kernel family, all computing the same
+ * result). FA_ERR_UNSUPPORTED if the variant does not exist for this
+ * dtype and D.
+ */
+int fa_fwd_variant(const void *q, const void *k, const void *v, void *o,
+                   float *lse, int64_t B, int64_t H, int64_t N, int64_t n_kv,
+                   int64_t D, int causal, float scale, int dtype, void *stream,
+                   int variant);
+
+/* Number of variants (see fa_fwd_variant) and a short name for each;
+ * the name of an unknown variant is "". */
+int fa_num_variants(void);
+const char *fa_variant_name(int variant);
+
+/* Static text for a status code. For FA_ERR_HIP it is the HIP error string
+ * of the most recent failure on the calling thread. Never NULL. */
+const char *fa_strerror(int code);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

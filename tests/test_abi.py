@@ -1,0 +1,114 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every
+function that include/*.h declares, and validates its arguments before any
+HIP call (so every error path can be exercised here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import exact_attention_10_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# fake, never dereferenced device addresses (validation runs before any HIP call)
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIBRARY):
+        pytest.fail("HIP library not built: run `python -m exact_attention_10_amd.build`")
+    return fa.load_library()
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
+              "fa_num_variants", "fa_variant_name"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+        assert n in fa.SIGNATURES, f"{n} has no binding signature"
+
+
+def test_version_and_strings(lib):
+    assert lib.fa_version() >= 100
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_ALIGNMENT,
+                 fa.FA_ERR_HIP, 12345):
+        assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
+    n = fa.fa_num_variants()
+    assert n >= 1
+    assert all(fa.fa_variant_name(i) for i in range(n))
+    assert fa.fa_variant_name(n) == "" and fa.fa_variant_name(-1) == ""
+
+
+def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, N=256, D=128, causal=0, scale=0.088,
+         dtype=fa.FA_DTYPE_BF16, n_kv=None, variant=None):
+    if variant is not None:
+        return lib.fa_fwd_variant(q, k, v, o, lse, B, H, N, N if n_kv is None else n_kv, D,
+                                  causal, scale, dtype, None, variant)
+    if n_kv is not None:
+        return lib.fa_fwd_nk(q, k, v, o, lse, B, H, N, n_kv, D, causal, scale, dtype, None)
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=Q + 8), fa.FA_ERR_ALIGNMENT),
+    (dict(lse=L + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(o=Q), fa.FA_ERR_INVALID_ARG),                 # output aliases an input
+    (dict(o=K + 4096), fa.FA_ERR_INVALID_ARG),          # partial overlap
+    (dict(lse=O + 64), fa.FA_ERR_INVALID_ARG),          # lse inside o
+    (dict(N=1 << 24, D=128, dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),  # head > 2 GiB
+    (dict(n_kv=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(n_kv=257), fa.FA_ERR_INVALID_ARG),
+    (dict(variant=99), fa.FA_ERR_UNSUPPORTED),
+    (dict(variant=-1), fa.FA_ERR_UNSUPPORTED),
+])
+def test_validation_rejects_before_any_hip_call(lib, kw, code):
+    assert call(lib, **kw) == code
+
+
+def test_lse_may_be_null_for_validation(lib):
+    # with lse = NULL, an otherwise invalid call still fails in validation
+    assert call(lib, lse=None, D=80) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        fa.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x, x, x)

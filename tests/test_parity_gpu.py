@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes are compared on every output element; the full-size workloads
+run in the launch configuration the benchmark times (fa_fwd, variant 0) and
+are compared on sampled rows that the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import exact_attention_10_amd as fa
+import fa_inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["fp32", "fp16", "bf16"]
+
+
+def _banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(qb, kb, vb, dtype, causal, scale, n_kv=None, variant=None):
+    import torch
+    q, k, v = (parity.to_device(x, dtype) for x in (qb, kb, vb))
+    if variant is not None:
+        o, lse = fa.fa_fwd_variant(q, k, v, causal=causal, scale=scale, variant=variant,
+                                   n_kv=n_kv)
+    elif n_kv is not None:
+        o, lse = fa.fa_fwd_nk(q, k, v, n_kv=n_kv, causal=causal, scale=scale)
+    else:
+        o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return parity.from_device(o), lse.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Small shapes, every element: several query/key tiles and ragged tails
+
+
+@pytest.mark.parametrize("N", [1, 37, 64, 127, 128, 129, 200, 383])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_small_full_parity(dtype, D, causal, N):
+    _banner(f"small dtype={dtype} D={D} causal={causal} N={N}")
+    B, H = 2, 3
+    seed = 1000 + N + D + (7 if causal else 0) + DTYPES.index(dtype)
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, seed)
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, dtype, causal, scale)
+    o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, causal)
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"{dtype} D={D} causal={causal} N={N}")
+
+
+@pytest.mark.parametrize("n_kv", [0, 1, 63, 64, 65, 150, 257])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_key_length_mask(dtype, causal, n_kv):
+    """Keys >= n_kv are invisible; n_kv = 0 leaves every row without a key:
+    O = 0 and LSE = -inf exactly (the guard for fully masked rows)."""
+    _banner(f"n_kv dtype={dtype} causal={causal} n_kv={n_kv}")
+    B, H, N, D = 1, 2, 257, 64
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 77 + n_kv)
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, dtype, causal, scale, n_kv=n_kv)
+    o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, causal, n_kv=n_kv)
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"n_kv={n_kv}")
+    if n_kv == 0:
+        assert (o == 0).all() and np.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("variant", range(2))
+@pytest.mark.parametrize("causal", [False, True])
+def test_variants(variant, causal):
+    if variant >= fa.fa_num_variants():
+        pytest.skip("variant not built")
+    _banner(f"variant {variant} ({fa.fa_variant_name(variant)}) causal={causal}")
+    B, H, N, D, dtype = 2, 4, 520, 128, "bf16"
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 500 + variant)
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, dtype, causal, scale, variant=variant)
+    o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, causal)
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"variant {variant}")
+    o0, l0 = _run(qb, kb, vb, dtype, causal, scale)
+    assert np.array_equal(o, o0) and np.array_equal(lse, l0), "variants differ from fa_fwd"
+
+
+def test_no_lse_output():
+    import torch
+    _banner("lse = NULL")
+    qb, kb, vb = fa_inputs.draw_qkv(1, 2, 300, 64, "bf16", 9)
+    q, k, v = (parity.to_device(x, "bf16") for x in (qb, kb, vb))
+    o, lse = fa.fa_fwd(q, k, v, causal=True, with_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    o_ref, _ = parity.reference_full(qb, kb, vb, "bf16", 1 / 8, True)
+    parity.check(parity.from_device(o), None, o_ref, None, "bf16", "no lse")
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants on the GPU
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_causal_first_row_is_first_value(dtype):
+    """Query 0 sees only key 0: O[0] = V[0] (bit-exact after rounding to a
+    16-bit output), LSE[0] = scale * q0 . k0."""
+    _banner(f"causal row 0 dtype={dtype}")
+    qb, kb, vb = fa_inputs.draw_qkv(2, 2, 200, 128, dtype, 31)
+    scale = parity.default_scale(128)
+    o, lse = _run(qb, kb, vb, dtype, True, scale)
+    v32 = fa_inputs.to_f32(vb, dtype)
+    q32, k32 = fa_inputs.to_f32(qb, dtype), fa_inputs.to_f32(kb, dtype)
+    for b in range(2):
+        for h in range(2):
+            if dtype == "fp32":
+                assert np.allclose(o[b, h, 0], v32[b, h, 0], rtol=4e-7, atol=0)
+            else:
+                assert np.array_equal(o[b, h, 0], v32[b, h, 0])
+            expect = scale * math.fsum(float(x) * float(y) for x, y in zip(q32[b, h, 0], k32[b, h, 0]))
+            assert abs(lse[b, h, 0] - expect) <= 1e-4 * max(1.0, abs(expect))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_means(causal):
+    """Q = 0: every visible score is 0, so O is the mean (causal: prefix mean)
+    of the value rows and LSE = log(number of visible keys)."""
+    _banner(f"Q=0 causal={causal}")
+    B, H, N, D, dtype = 1, 2, 333, 64, "bf16"
+    _, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 41)
+    qb = np.zeros_like(kb)
+    o, lse = _run(qb, kb, vb, dtype, causal, 0.125)
+    v = fa_inputs.to_f32(vb, dtype).astype(np.float64)
+    if causal:
+        ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+        lref = np.log(np.arange(1, N + 1))[None, None, :]
+    else:
+        ref = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        lref = np.full((1, 1, N), math.log(N))
+    assert np.abs(o - ref).max() <= parity.TOL_O_16
+    assert np.abs(lse - lref).max() <= parity.TOL_LSE
+
+
+def test_key_permutation_invariance():
+    _banner("key permutation")
+    B, H, N, D, dtype = 1, 2, 300, 128, "fp16"
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 51)
+    perm = np.random.default_rng(52).permutation(N)
+    o1, l1 = _run(qb, kb, vb, dtype, False, 0.09)
+    o2, l2 = _run(qb, kb[:, :, perm].copy(), vb[:, :, perm].copy(), dtype, False, 0.09)
+    assert np.abs(o1 - o2).max() <= parity.TOL_O_16
+    assert np.abs(l1 - l2).max() <= parity.TOL_LSE
+
+
+@pytest.mark.parametrize("q_mult", [8.0, 32.0])
+def test_amplified_scores_stay_finite(q_mult):
+    """Large score spreads stress the running-max rescale ("Building a
+    Verifiable FlashAttention Forward", Part 4)."""
+    _banner(f"amplified Q x{q_mult}")
+    B, H, N, D, dtype = 1, 4, 513, 128, "bf16"
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 61, q_mult=q_mult, v_dist="uniform")
+    for causal in (False, True):
+        o, lse = _run(qb, kb, vb, dtype, causal, parity.default_scale(D))
+        o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, parity.default_scale(D), causal)
+        parity.check(o, lse, o_ref, lse_ref, dtype, f"amplified x{q_mult} causal={causal}")
+
+
+def test_bitwise_deterministic():
+    _banner("determinism")
+    qb, kb, vb = fa_inputs.draw_qkv(2, 8, 1000, 128, "bf16", 71)
+    runs = [_run(qb, kb, vb, "bf16", c, 0.0884) for c in (False, True, False, True)]
+    assert np.array_equal(runs[0][0], runs[2][0]) and np.array_equal(runs[0][1], runs[2][1])
+    assert np.array_equal(runs[1][0], runs[3][0]) and np.array_equal(runs[1][1], runs[3][1])
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size, in the benchmark's launch configuration
+
+
+WORKLOAD_CASES = [(name, c) for name, w in fa_inputs.WORKLOADS.items() for c in w.masks]
+
+
+@pytest.mark.parametrize("name,causal", WORKLOAD_CASES,
+                         ids=[f"{n}-{'causal' if c else 'full'}" for n, c in WORKLOAD_CASES])
+def test_workload_full_size(name, causal):
+    w = fa_inputs.WORKLOADS[name]
+    _banner(f"workload {name} causal={causal}")
+    qb, kb, vb = fa_inputs.workload_inputs(w)
+    o, lse = _run(qb, kb, vb, w.dtype, causal, w.scale)
+    if w.B * w.H * w.N <= 4096:
+        o_ref, lse_ref = parity.reference_full(qb, kb, vb, w.dtype, w.scale, causal)
+        parity.check(o, lse, o_ref, lse_ref, w.dtype, name)
+        return
+    rows = parity.sample_rows(w.B, w.H, w.N, 384, seed=w.seed)
+    o_ref, lse_ref = parity.reference_rows(qb, kb, vb, w.dtype, w.scale, causal, rows)
+    o2 = o.reshape(w.B * w.H, w.N, w.D)[rows[:, 0], rows[:, 1]]
+    l2 = lse.reshape(w.B * w.H, w.N)[rows[:, 0], rows[:, 1]]
+    oe, le = parity.check(o2, l2, o_ref, lse_ref, w.dtype, name)
+    print(f"[parity] {name} causal={causal} rows={len(rows)} O err {oe:.3e} LSE err {le:.3e}",
+          flush=True)
+    # every output row is finite, and (non-degenerate inputs) LSE >= the row max
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
