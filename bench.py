@@ -81,7 +81,7 @@ def time_gpu(w, causal, steps, warmup, torch, fa):
             "flops": flops}
 
 
-def cpu_baseline(w, causal, target_s=12.0):
+def cpu_baseline(w, causal, target_s=15.0):
     """The fp64 oracle on a bounded sample of rows of the same workload."""
     import oracle
     threads = len(os.sched_getaffinity(0))
@@ -98,7 +98,7 @@ def cpu_baseline(w, causal, target_s=12.0):
         oracle.attention_rows(q, k, v, w.scale, causal, rows)
         return time.perf_counter() - t0, flops
 
-    probe_rows = 64
+    probe_rows = 2048
     t, f = run(probe_rows)
     n_rows = int(min(1 << 20, max(probe_rows, probe_rows * target_s / max(t, 1e-3))))
     t, f = run(n_rows)
@@ -116,7 +116,21 @@ def main():
     ap.add_argument("--workload", default=fa_inputs.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times) to calibrate "
+                         "HBM byte counters, then exit")
     a = ap.parse_args()
+
+    if a.copy_calibration:
+        import torch
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 5}), flush=True)
+        return
 
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the attention "

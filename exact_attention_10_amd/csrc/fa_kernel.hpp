@@ -45,10 +45,17 @@ typedef short s16x4 __attribute__((vector_size(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define FA_LDS __attribute__((address_space(3)))
 
 enum { DT_FP32 = 0, DT_FP16 = 1, DT_BF16 = 2 };
+
+// The exponent reference of a row is moved only when the row max exceeds it
+// by more than this many powers of two (so every p is at most 2^8).
+constexpr float kRescaleSlack = 8.0f;
 
 struct Params {
   const void *q, *k, *v;
@@ -81,7 +88,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 // vmcnt(0): wait until this wave's outstanding vector-memory operations,
 // including LDS-direct loads, have completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_base + 16*i; reads at offsets beyond the resource's range return 0.
+// Issued as inline asm so that the compiler does not treat the transfer as an
+// outstanding LDS write that every later LDS read must wait for: the kernel
+// orders these transfers itself (wait_vmem + barrier before a tile is read).
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+__device__ __forceinline__ i32x4 make_rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);   // stride 0
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
 
 // Max over the two 32-lane halves: both halves end with the same value.
 __device__ __forceinline__ float halves_max(float x) {
@@ -93,6 +121,15 @@ __device__ __forceinline__ float halves_sum(float x) {
   u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
       __float_as_uint(x), __float_as_uint(x), false, false));
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two fp32 values rounded to nearest-even into one packed 16-bit pair
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float x0, float x1) {
+  const f32x2 v = {x0, x1};
+  if constexpr (DT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
 // LDS row swizzle: the 16-byte chunk c of tile row r is stored at chunk
@@ -173,8 +210,10 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
   constexpr int QE = KSTEP / 2;             // elements per lane per fragment
   typedef uint16_t qraw_t __attribute__((ext_vector_type(8)));
   const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(head_elems * ES));
-  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kh, (uint32_t)((int64_t)n_kv * D * ES));
-  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vh, (uint32_t)((int64_t)n_kv * D * ES));
+  // wave-uniform resources (kept in SGPRs) for the K and V tile transfers
+  const i32x4 k_rsrc = make_rsrc_words(kh, (uint32_t)((int64_t)n_kv * D * ES));
+  const i32x4 v_rsrc = make_rsrc_words(vh, (uint32_t)((int64_t)n_kv * D * ES));
+  const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
   // fragments stored as raw 32-bit words
   constexpr int QW = (QE * ES) / 4;          // 32-bit words per Q fragment
@@ -196,11 +235,15 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
     }
   }
 
+  // Q is needed in every iteration: complete its loads here, so that no wait
+  // for them is left inside the loop (where it would also wait for prefetches).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
   // ---- K/V tile staging: direct global->LDS loads into a swizzled layout ----
   auto issue_tile = [&](int t, int buf) {
     const int kstart = t * BN;
-    char *kl = smem + buf * (2 * C::TILE_BYTES);
-    char *vl = kl + C::TILE_BYTES;
+    const uint32_t kl = smem_base + buf * (2 * C::TILE_BYTES);
+    const uint32_t vl = kl + C::TILE_BYTES;
 #pragma unroll
     for (int u = 0; u < C::LOADS_PER_THREAD; ++u) {
       const int inst = wave * C::LOADS_PER_THREAD + u;          // 1 KB of LDS each
@@ -209,8 +252,8 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
       const int pchunk = (lds_off % RB) / 16;
       const int lchunk = pchunk ^ swz<RB>(row);
       const uint32_t goff = (uint32_t)(kstart + row) * RB + lchunk * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (FA_LDS void *)(kl + inst * 1024), 16, goff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (FA_LDS void *)(vl + inst * 1024), 16, goff, 0, 0, 0);
+      lds_dma16(k_rsrc, goff, kl + inst * 1024);
+      lds_dma16(v_rsrc, goff, vl + inst * 1024);
     }
   };
 
@@ -218,7 +261,7 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;     // running max (base-2 units), same in both halves
+  float m_run = -INFINITY;     // exponent reference (base-2 units), same in both halves
   float l_run = 0.f;           // this lane's partial row sum (its half's keys)
   const float c = p.c;
 
@@ -236,14 +279,17 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
     const char *vl = kl + C::TILE_BYTES;
 
     // ---- S^T = K Q^T : NKB blocks of 32 keys x 32 queries ----
+    // head-dim chunks outer, key blocks inner, so consecutive MFMAs feed
+    // independent accumulators
     f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + l32;
-      const char *rowp = kl + row * RB;
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + l32;
+        const char *rowp = kl + row * RB;
         if constexpr (DT == DT_FP32) {
           const int col = kc * 2 + half;                       // element
           const int ch = (col / 4) ^ swz<RB>(row);
@@ -275,16 +321,33 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
     }
 
     // ---- online softmax ----
+    // m_run is the exponent reference shared by l and acc (base-2 units).
+    // It moves to the running max only when some row of the wave has a new
+    // max more than kRescaleSlack above it; until then the stale reference
+    // is kept and p = exp2(s*c - m_run) stays below 2^kRescaleSlack. Any
+    // common reference gives the same acc / l and m_run + log2 l ("A09",
+    // section 3: rebasing multiplies every accumulated term by one common
+    // factor), so this skips most accumulator rescales without changing the
+    // result beyond rounding.
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    const float neg = -m_ref;
+    mx = halves_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      // alpha = 0 on the first visible tile (m_run = -inf), 1 if unchanged
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+    // a row that has seen no visible key has only -inf scores: p = 0
+    const float neg = (m_run == -INFINITY) ? 0.f : -m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -294,16 +357,7 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
         s[kb][i] = e;
         rs += e;
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    // alpha is exactly 1 when the max did not move; skip the rescale when that
-    // holds for every lane of the wave (the product would be unchanged).
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-    }
+    l_run += rs;
 
     // ---- O^T += V^T P^T ----
     if constexpr (DT == DT_FP32) {
@@ -328,16 +382,7 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
         const int kb = pc / 2, i0 = (pc % 2) * 8;
         u32x4 b;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float x0 = s[kb][i0 + 2 * w], x1 = s[kb][i0 + 2 * w + 1];
-          if constexpr (DT == DT_BF16) {
-            __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
-            b[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          } else {
-            _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-            b[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          }
-        }
+        for (int w = 0; w < 4; ++w) b[w] = pack2<DT>(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
         // V^T operand for lane (d = db*32 + l32, half): V[k0 + 0..3][d] and
         // V[k0 + 8 + 0..3][d], k0 = pc*16 + half*4, via the transposing read:
         // within each 16-lane group, lane g16 = 4*r + cq addresses row k + r,
@@ -382,19 +427,9 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
                       acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
           *(float4 *)(orow + d0 * 4) = w;
         } else {
-          uint32_t w[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float x0 = acc[db][gq * 4 + 2 * h] * inv, x1 = acc[db][gq * 4 + 2 * h + 1] * inv;
-            if constexpr (DT == DT_BF16) {
-              __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
-              w[h] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-            } else {
-              _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-              w[h] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-            }
-          }
-          *(u32x2 *)(orow + d0 * 2) = u32x2{w[0], w[1]};
+          const uint32_t w0 = pack2<DT>(acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv);
+          const uint32_t w1 = pack2<DT>(acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv);
+          *(u32x2 *)(orow + d0 * 2) = u32x2{w0, w1};
         }
       }
     if (p.lse && half == 0) {
