@@ -57,21 +57,29 @@ def _device_inputs(w, torch):
     return (dev(qb), dev(kb), dev(vb)), (qb, kb, vb)
 
 
-def time_gpu(w, causal, steps, warmup, torch, fa):
-    """Median-free whole-run timing: `warmup` untimed calls, then `steps` calls
-    bracketed by synchronisation and events on the launch stream."""
+def time_gpu(w, causal, steps, warmup, torch, fa, variant=None):
+    """Whole-run timing: `warmup` untimed calls, then `steps` calls bracketed
+    by synchronisation and events on the launch stream (fa_fwd, or kernel
+    variant `variant` through fa_fwd_variant)."""
     (q, k, v), _ = _device_inputs(w, torch)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
+
+    def call():
+        if variant is None:
+            fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+        else:
+            fa.fa_fwd_variant(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream,
+                              variant=variant)
     for _ in range(warmup):
-        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+        call()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
-        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+        call()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -116,6 +124,8 @@ def main():
     ap.add_argument("--workload", default=fa_inputs.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--sweep-variants", action="store_true",
+                    help="time every kernel variant on the N=4096 workloads and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) to calibrate "
                          "HBM byte counters, then exit")
@@ -146,6 +156,20 @@ def main():
         sys.exit(1)
 
     w = fa_inputs.WORKLOADS[a.workload]
+    if a.sweep_variants:
+        for name in (w.name, "b4h16_n4096_d64_bf16", "b1h32_n16384_d128_bf16_q8"):
+            wl = fa_inputs.WORKLOADS[name]
+            for causal in wl.masks:
+                for var in range(fa.fa_num_variants()):
+                    try:
+                        r = time_gpu(wl, causal, a.steps, a.warmup, torch, fa, variant=var)
+                    except fa.FAError as e:
+                        print(f"[sweep] {name} causal={causal} {fa.fa_variant_name(var)}: {e}",
+                              flush=True)
+                        continue
+                    print(f"[sweep] {name} causal={int(causal)} {fa.fa_variant_name(var):28s} "
+                          f"{r['ms']:.4f} ms {r['tflops']:7.1f} TFLOP/s", flush=True)
+        return
     head = time_gpu(w, False, a.steps, a.warmup, torch, fa)
     print(f"[bench] {w.name} non-causal: {head['ms']:.4f} ms/step {head['tflops']:.1f} TFLOP/s",
           file=sys.stderr, flush=True)

@@ -16,7 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libfa_mi355x.so")
 SOURCES = [os.path.join(CSRC, "fa_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "fa_kernel.hpp"), os.path.join(ROOT, "include", "fa.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, "fa_kernel.hpp"), os.path.join(CSRC, "fa_kernel_pingpong.hpp"),
+                     os.path.join(CSRC, "fa_kernel_interleaved.hpp"),
+                     os.path.join(ROOT, "include", "fa.h")]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for device code (a host-pass warning about

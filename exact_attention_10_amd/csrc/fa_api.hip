@@ -7,6 +7,8 @@
 // the caller's stream.
 #include "fa.h"
 #include "fa_kernel.hpp"
+#include "fa_kernel_pingpong.hpp"
+#include "fa_kernel_interleaved.hpp"
 
 #include <cmath>
 #include <cstdio>
@@ -19,52 +21,78 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
+enum Family { kSimple = 0, kPingPong = 1, kInterleaved = 2 };
+
 struct Variant {
   const char *name;
+  int family;      // kernel family; 16-bit inputs only for kPingPong
   int xcd_remap;
 };
 
-// Variants of the same kernel family; 0 is what fa_fwd runs.
+// Variants of the same computation; 0 is what fa_fwd runs (the fastest
+// measured family for every dtype).
 const Variant kVariants[] = {
-    {"bm128_bn64_xcd", 1},
-    {"bm128_bn64_linear", 0},
+    {"default", -1, 1},
+    {"simple_bm128_xcd", kSimple, 1},
+    {"simple_bm128_linear", kSimple, 0},
+    {"pingpong_bm256_xcd", kPingPong, 1},
+    {"pingpong_bm256_linear", kPingPong, 0},
+    {"interleaved_bm128_xcd", kInterleaved, 1},
+    {"interleaved_bm128_linear", kInterleaved, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
-using KernelFn = void (*)(fa::Params);
-
-template <int DT, int D, bool CAUSAL>
-struct Inst {
-  static const void *fn() { return reinterpret_cast<const void *>(&fa::fa_fwd_kernel<DT, D, CAUSAL>); }
-  static constexpr int lds = fa::Cfg<DT, D, CAUSAL>::LDS_BYTES;
-  static constexpr int bm = fa::Cfg<DT, D, CAUSAL>::BM;
-};
 
 struct Launch {
   const void *fn;
   int lds;
   int bm;
+  int threads;
 };
 
-template <int DT, int D>
-Launch pick_causal(int causal) {
-  if (causal) return {Inst<DT, D, true>::fn(), Inst<DT, D, true>::lds, Inst<DT, D, true>::bm};
-  return {Inst<DT, D, false>::fn(), Inst<DT, D, false>::lds, Inst<DT, D, false>::bm};
+template <int DT, int D, bool CAUSAL>
+Launch simple_launch() {
+  return {reinterpret_cast<const void *>(&fa::fa_fwd_kernel<DT, D, CAUSAL>),
+          fa::Cfg<DT, D, CAUSAL>::LDS_BYTES, fa::Cfg<DT, D, CAUSAL>::BM, 256};
 }
 
-bool pick(int dtype, int64_t D, int causal, Launch *out) {
+template <int DT, int D, bool CAUSAL>
+Launch pingpong_launch() {
+  return {reinterpret_cast<const void *>(&fa::fa_fwd_pingpong_kernel<DT, D, CAUSAL>),
+          fa::PPCfg<DT, D, CAUSAL>::LDS_BYTES, fa::PPCfg<DT, D, CAUSAL>::BM, 512};
+}
+
+template <int DT, int D, bool CAUSAL>
+Launch interleaved_launch() {
+  return {reinterpret_cast<const void *>(&fa::fa_fwd_interleaved_kernel<DT, D, CAUSAL>),
+          fa::IWCfg<DT, D, CAUSAL>::LDS_BYTES, fa::IWCfg<DT, D, CAUSAL>::BM, 256};
+}
+
+template <int DT, int D>
+Launch pick_dt_d(int family, int causal) {
+  if constexpr (DT != fa::DT_FP32) {
+    if (family == kPingPong)
+      return causal ? pingpong_launch<DT, D, true>() : pingpong_launch<DT, D, false>();
+    if (family == kInterleaved)
+      return causal ? interleaved_launch<DT, D, true>() : interleaved_launch<DT, D, false>();
+  }
+  return causal ? simple_launch<DT, D, true>() : simple_launch<DT, D, false>();
+}
+
+bool pick(int dtype, int64_t D, int causal, int family, Launch *out) {
+  if (family == -1) family = kSimple;
+  if (family != kSimple && dtype == FA_DTYPE_FP32) return false;
   switch (dtype) {
     case FA_DTYPE_BF16:
-      if (D == 64) { *out = pick_causal<fa::DT_BF16, 64>(causal); return true; }
-      if (D == 128) { *out = pick_causal<fa::DT_BF16, 128>(causal); return true; }
+      if (D == 64) { *out = pick_dt_d<fa::DT_BF16, 64>(family, causal); return true; }
+      if (D == 128) { *out = pick_dt_d<fa::DT_BF16, 128>(family, causal); return true; }
       return false;
     case FA_DTYPE_FP16:
-      if (D == 64) { *out = pick_causal<fa::DT_FP16, 64>(causal); return true; }
-      if (D == 128) { *out = pick_causal<fa::DT_FP16, 128>(causal); return true; }
+      if (D == 64) { *out = pick_dt_d<fa::DT_FP16, 64>(family, causal); return true; }
+      if (D == 128) { *out = pick_dt_d<fa::DT_FP16, 128>(family, causal); return true; }
       return false;
     case FA_DTYPE_FP32:
-      if (D == 64) { *out = pick_causal<fa::DT_FP32, 64>(causal); return true; }
-      if (D == 128) { *out = pick_causal<fa::DT_FP32, 128>(causal); return true; }
+      if (D == 64) { *out = pick_dt_d<fa::DT_FP32, 64>(family, causal); return true; }
+      if (D == 128) { *out = pick_dt_d<fa::DT_FP32, 128>(family, causal); return true; }
       return false;
     default:
       return false;
@@ -111,6 +139,8 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse,
   return FA_OK;
 }
 
+void opt_in_lds(const void *fn, int bytes);
+
 int launch(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D, int causal,
            float scale, int dtype, void *stream, int variant) {
@@ -118,7 +148,8 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   if (rc != FA_OK) return rc;
   if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
   Launch L;
-  if (!pick(dtype, D, causal, &L)) return FA_ERR_UNSUPPORTED;
+  if (!pick(dtype, D, causal, kVariants[variant].family, &L)) return FA_ERR_UNSUPPORTED;
+  if (L.lds > 65536) opt_in_lds(L.fn, L.lds);
 
   fa::Params p;
   p.q = q;
@@ -134,7 +165,7 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   p.c = (float)((double)scale * 1.4426950408889634);
 
   const dim3 grid((unsigned)(B * H * p.nq_tiles));
-  const dim3 block(256);
+  const dim3 block((unsigned)L.threads);
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(L.fn, grid, block, args, (size_t)L.lds,
                                  reinterpret_cast<hipStream_t>(stream));
@@ -145,20 +176,17 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   return FA_OK;
 }
 
-// Kernels that use more than 64 KB of LDS must opt in once per process.
-struct LdsOptIn {
-  static void apply() {
-    static std::once_flag once;
-    std::call_once(once, [] {
-    (void)hipFuncSetAttribute(Inst<fa::DT_FP32, 128, false>::fn(),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Inst<fa::DT_FP32, 128, false>::lds);
-    (void)hipFuncSetAttribute(Inst<fa::DT_FP32, 128, true>::fn(),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Inst<fa::DT_FP32, 128, true>::lds);
-    });
-  }
-};
+// Kernels that use more than 64 KB of LDS raise their limit once per process.
+void opt_in_lds(const void *fn, int bytes) {
+  static std::mutex mu;
+  static const void *done[32];
+  static int n_done = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n_done; ++i)
+    if (done[i] == fn) return;
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (n_done < 32) done[n_done++] = fn;
+}
 
 }  // namespace
 
@@ -167,9 +195,6 @@ extern "C" {
 int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse,
                    int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D,
                    int causal, float scale, int dtype, void *stream, int variant) {
-  int rc = validate(q, k, v, o, lse, B, H, N, n_kv, D, scale, dtype);
-  if (rc != FA_OK) return rc;
-  if (dtype == FA_DTYPE_FP32 && D == 128) LdsOptIn::apply();
   return launch(q, k, v, o, lse, B, H, N, n_kv, D, causal, scale, dtype, stream, variant);
 }
 

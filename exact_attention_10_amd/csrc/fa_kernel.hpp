@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -96,8 +98,13 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // outstanding LDS write that every later LDS read must wait for: the kernel
 // orders these transfers itself (wait_vmem + barrier before a tile is read).
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds_base) {
+  // the resource and the LDS base are wave-uniform; make that explicit so
+  // they live in scalar registers as the instruction requires
+  i32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rsrc)
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(r)
                : "memory");
 }
 
@@ -210,9 +217,6 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
   constexpr int QE = KSTEP / 2;             // elements per lane per fragment
   typedef uint16_t qraw_t __attribute__((ext_vector_type(8)));
   const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(head_elems * ES));
-  // wave-uniform resources (kept in SGPRs) for the K and V tile transfers
-  const i32x4 k_rsrc = make_rsrc_words(kh, (uint32_t)((int64_t)n_kv * D * ES));
-  const i32x4 v_rsrc = make_rsrc_words(vh, (uint32_t)((int64_t)n_kv * D * ES));
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
   // fragments stored as raw 32-bit words
@@ -240,22 +244,57 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- K/V tile staging: direct global->LDS loads into a swizzled layout ----
-  auto issue_tile = [&](int t, int buf) {
+  // Each thread moves LOADS_PER_THREAD fixed 16-byte pieces of the K tile and
+  // of the V tile. A piece's offset relative to the tile's first row does not
+  // change from tile to tile, so per tile only the (scalar) buffer resource
+  // moves: its base is the tile's first row and its range ends at key n_kv,
+  // so rows past the keys read as zeros.
+  uint32_t dma_off[C::LOADS_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < C::LOADS_PER_THREAD; ++u) {
+    const int lds_off = (wave * C::LOADS_PER_THREAD + u) * 1024 + lane * 16;
+    const int row = lds_off / RB;
+    dma_off[u] = (uint32_t)row * RB + (((lds_off % RB) / 16) ^ swz<RB>(row)) * 16;
+  }
+  auto issue_tile = [&](int t, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     const int kstart = t * BN;
-    const uint32_t kl = smem_base + buf * (2 * C::TILE_BYTES);
-    const uint32_t vl = kl + C::TILE_BYTES;
+    const uint32_t valid = (uint32_t)(n_kv - kstart) * RB;      // kstart < n_kv here
+    const i32x4 kr = make_rsrc_words(kh + (int64_t)kstart * RB, valid);
+    const i32x4 vr = make_rsrc_words(vh + (int64_t)kstart * RB, valid);
 #pragma unroll
     for (int u = 0; u < C::LOADS_PER_THREAD; ++u) {
-      const int inst = wave * C::LOADS_PER_THREAD + u;          // 1 KB of LDS each
-      const int lds_off = inst * 1024 + lane * 16;
-      const int row = lds_off / RB;
-      const int pchunk = (lds_off % RB) / 16;
-      const int lchunk = pchunk ^ swz<RB>(row);
-      const uint32_t goff = (uint32_t)(kstart + row) * RB + lchunk * 16;
-      lds_dma16(k_rsrc, goff, kl + inst * 1024);
-      lds_dma16(v_rsrc, goff, vl + inst * 1024);
+      const uint32_t lds = smem_base + buf * (2 * C::TILE_BYTES) + (wave * C::LOADS_PER_THREAD + u) * 1024;
+      lds_dma16(kr, dma_off[u], lds);
+      lds_dma16(vr, dma_off[u], lds + C::TILE_BYTES);
     }
   };
+
+  // Lane offsets of the 16-bit MFMA operand fragments inside a tile. The
+  // swizzle of a row depends only on its low 4 bits, so the fragment of key
+  // block kb (K) or key chunk pc (V) is the offset of block 0 plus a
+  // compile-time constant, and every LDS read is one register plus an
+  // immediate offset.
+  constexpr int NKO = (DT == DT_FP32) ? 1 : NKC;
+  constexpr int NVO = (DT == DT_FP32) ? 1 : NDB;
+  uint32_t k_off[NKO], v_off[2][NVO];
+  if constexpr (DT != DT_FP32) {
+    const int g = lane >> 4, r = (lane & 15) >> 2, cq = lane & 3;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) k_off[kc] = l32 * RB + (((kc * 2 + half) ^ swz<RB>(l32)) * 16);
+#pragma unroll
+    for (int jg = 0; jg < 2; ++jg)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        // V^T operand for lane (d = db*32 + l32, half): V[k0 + 0..3][d] and
+        // V[k0 + 8 + 0..3][d], k0 = pc*16 + half*4, via the transposing read:
+        // within each 16-lane group, lane 4*r + cq addresses row k + r,
+        // head-dim columns 4*cq .. 4*cq+3 of the group's 16 columns.
+        const int col = db * 32 + (g & 1) * 16 + cq * 4;
+        const int key = jg * 8 + (g >> 1) * 4 + r;
+        v_off[jg][db] = key * RB + ((((col * 2) / 16) ^ swz<RB>(key)) * 16) + (col * 2) % 16;
+      }
+  }
 
   // ---- running state ----
   f32x16 acc[NDB];
@@ -265,46 +304,73 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
   float l_run = 0.f;           // this lane's partial row sum (its half's keys)
   const float c = p.c;
 
-  if (n_tiles > 0) issue_tile(0, 0);
-
-  for (int t = 0; t < n_tiles; ++t) {
+  // one key tile; buf (0 or 1) is a compile-time constant so that every LDS
+  // address is a register plus an immediate
+  auto step = [&](int t, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     wait_vmem();
-    __syncthreads();                        // tile t visible; buffer (t+1)&1 free
-    if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+    __syncthreads();                        // tile t visible; the other buffer is free
+    if (t + 1 < n_tiles) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
 
     const int kstart = t * BN;
-    if (CAUSAL && kstart > qw + 31) continue;   // every key of this tile is in this wave's future
+    if (CAUSAL && kstart > qw + 31) return;   // every key of this tile is in this wave's future
 
-    const char *kl = smem + (t & 1) * (2 * C::TILE_BYTES);
+    const char *kl = smem + buf * (2 * C::TILE_BYTES);
     const char *vl = kl + C::TILE_BYTES;
 
     // ---- S^T = K Q^T : NKB blocks of 32 keys x 32 queries ----
     // head-dim chunks outer, key blocks inner, so consecutive MFMAs feed
-    // independent accumulators
+    // independent accumulators. For 16-bit inputs all K fragments are read
+    // up front so the MFMAs wait only for the first one.
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    if constexpr (DT == DT_FP32) {
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
+      for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int row = kb * 32 + l32;
-        const char *rowp = kl + row * RB;
-        if constexpr (DT == DT_FP32) {
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int row = kb * 32 + l32;
           const int col = kc * 2 + half;                       // element
           const int ch = (col / 4) ^ swz<RB>(row);
-          const float a = *(const FA_LDS float *)(rowp + ch * 16 + (col % 4) * 4);
+          const float a = *(const FA_LDS float *)(kl + row * RB + ch * 16 + (col % 4) * 4);
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, __uint_as_float(qf[kc][0]), s[kb], 0, 0, 0);
-        } else {
-          const int ch = (kc * 2 + half) ^ swz<RB>(row);
-          const u32x4 a = *(const FA_LDS u32x4 *)(rowp + ch * 16);
-          u32x4 b = {qf[kc][0], qf[kc][1], qf[kc][2], qf[kc][3]};
-          if constexpr (DT == DT_BF16)
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), s[kb], 0, 0, 0);
-          else
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), s[kb], 0, 0, 0);
         }
-      }
+    } else {
+      u32x4 kf[NKC][NKB];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kf[kc][kb] = *(const FA_LDS u32x4 *)(kl + k_off[kc] + kb * 32 * RB);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const u32x4 b = {qf[kc][0], qf[kc][1], qf[kc][2], qf[kc][3]};
+          if constexpr (DT == DT_BF16)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kc][kb]), __builtin_bit_cast(bf16x8, b), s[kb], 0, 0, 0);
+          else
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[kc][kb]), __builtin_bit_cast(f16x8, b), s[kb], 0, 0, 0);
+        }
+    }
+
+    // V^T fragments for this tile's PV, read now so that they arrive while
+    // the softmax runs (16-bit inputs)
+    constexpr int NVF = (DT == DT_FP32) ? 1 : NPC;
+    u32x4 vf[NVF][NVO];
+    if constexpr (DT != DT_FP32) {
+#pragma unroll
+      for (int pc = 0; pc < NPC; ++pc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int jg = 0; jg < 2; ++jg) {
+            const char *addr = vl + v_off[jg][db] + pc * 16 * RB;
+            const u32x2 xx = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)addr));
+            vf[pc][db][jg * 2] = xx[0];
+            vf[pc][db][jg * 2 + 1] = xx[1];
+          }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- masks: only on tiles past the end of the keys or on the diagonal ----
@@ -383,26 +449,9 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
         u32x4 b;
 #pragma unroll
         for (int w = 0; w < 4; ++w) b[w] = pack2<DT>(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
-        // V^T operand for lane (d = db*32 + l32, half): V[k0 + 0..3][d] and
-        // V[k0 + 8 + 0..3][d], k0 = pc*16 + half*4, via the transposing read:
-        // within each 16-lane group, lane g16 = 4*r + cq addresses row k + r,
-        // head-dim columns 4*cq .. 4*cq+3 of the group's 16 columns.
-        const int g = lane >> 4, g16 = lane & 15;
-        const int r = g16 >> 2, cq = g16 & 3;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int col = db * 32 + (g & 1) * 16 + cq * 4;        // element column
-          u32x4 a;
-#pragma unroll
-          for (int jg = 0; jg < 2; ++jg) {
-            const int key = pc * 16 + jg * 8 + (g >> 1) * 4 + r;
-            const int ch = ((col * 2) / 16) ^ swz<RB>(key);
-            const char *addr = vl + key * RB + ch * 16 + (col * 2) % 16;
-            s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)addr);
-            u32x2 xx = __builtin_bit_cast(u32x2, x);
-            a[jg * 2] = xx[0];
-            a[jg * 2 + 1] = xx[1];
-          }
+          const u32x4 a = vf[pc][db];
           if constexpr (DT == DT_BF16)
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[db], 0, 0, 0);
           else
@@ -410,6 +459,12 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
         }
       }
     }
+  };
+
+  if (n_tiles > 0) issue_tile(0, std::integral_constant<int, 0>{});
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- finalize: O = acc / l, LSE = (m + log2 l) ln 2 ----
