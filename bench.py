@@ -45,6 +45,42 @@ def attention_bytes(B, H, N, D, esize, with_lse=True):
     return 4 * B * H * N * D * esize + (4 * B * H * N if with_lse else 0)
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_kernel_bf16_d128_b4h16_n4096_hbm_traffic.txt")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources and build flags of the library, so a stored
+    counter reading is only used for the kernel it was taken on."""
+    import hashlib
+    from exact_attention_10_amd import build as fa_build
+    h = hashlib.sha256()
+    for path in sorted(fa_build.DEPENDS):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(fa_build.HIPCC_FLAGS).encode())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the headline kernel from the committed
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel sources changed
+    since the counters were taken (or no summary exists)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def _device_inputs(w, torch):
     qb, kb, vb = fa_inputs.workload_inputs(w)
     dt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
@@ -193,7 +229,7 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": stored_traffic(),
         "algorithmic_flops_per_launch": head["flops"],
         "algorithmic_bytes_per_launch": attention_bytes(w.B, w.H, w.N, w.D, esize),
         "kernel": "fa_fwd_kernel<bf16, D=128, non-causal>",
