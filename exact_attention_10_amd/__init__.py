@@ -54,6 +54,11 @@ def load_library(path: str = LIBRARY):
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m exact_attention_10_amd.build`")
+    # PyTorch ships its own HIP and HSA runtimes. Import it first so that the
+    # library binds to the runtime already in the process (same soname)
+    # instead of loading the system copies next to torch's: two HSA runtimes
+    # in one process do not share the device, and launches then fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

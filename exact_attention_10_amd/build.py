@@ -1,30 +1,34 @@
 """Build the gfx950 HIP library in-tree with hipcc.
 
 ``python -m exact_attention_10_amd.build`` compiles ``csrc/*.hip`` into
-``libfa_mi355x.so`` next to this file. ``--save-temps DIR`` also keeps the
-device assembly for inspection.
+``libfa_mi355x.so`` next to this file: each translation unit (the host API and
+one file per kernel family) is compiled to an object in parallel, then the
+objects are linked. ``--save-temps DIR`` also keeps the device assembly for
+inspection.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libfa_mi355x.so")
-SOURCES = [os.path.join(CSRC, "fa_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "fa_kernel.hpp"), os.path.join(CSRC, "fa_kernel_pingpong.hpp"),
-                     os.path.join(CSRC, "fa_kernel_interleaved.hpp"),
-                     os.path.join(ROOT, "include", "fa.h")]
+SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+DEPENDS = SOURCES + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [
+    os.path.join(ROOT, "include", "fa.h")]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for device code (a host-pass warning about
 # the unknown feature is expected and harmless).
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
@@ -37,19 +41,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(output: str = LIBRARY, save_temps: str | None = None, verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", output, *SOURCES]
-    if save_temps:
-        os.makedirs(save_temps, exist_ok=True)
-        cmd.insert(1, f"-save-temps={save_temps}" if False else "-save-temps")
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    cwd = save_temps if save_temps else None
+def _run(cmd, cwd=None):
     res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
     if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
+        sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+
+
+def build(output: str = LIBRARY, save_temps: str | None = None, verbose: bool = False,
+          jobs: int | None = None) -> str:
+    """Compile every translation unit in parallel and link the shared library.
+    The library is written to a temporary name and renamed into place, so a
+    failed build never leaves a partial file behind."""
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    objdir = tempfile.mkdtemp(prefix="fa_build_")
+    base = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    if save_temps:
+        os.makedirs(save_temps, exist_ok=True)
+        base.insert(1, "-save-temps")
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append(base + ["-c", "-o", obj, src])
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, save_temps) for c in cmds]:
+            f.result()
+    tmp = output + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, output)
+    for o in objs:
+        os.unlink(o)
+    os.rmdir(objdir)
     return output
 
 

@@ -7,8 +7,7 @@
 // the caller's stream.
 #include "fa.h"
 #include "fa_kernel.hpp"
-#include "fa_kernel_pingpong.hpp"
-#include "fa_kernel_interleaved.hpp"
+#include "fa_launch.hpp"
 
 #include <cmath>
 #include <cstdio>
@@ -42,61 +41,21 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-struct Launch {
-  const void *fn;
-  int lds;
-  int bm;
-  int threads;
-};
-
-template <int DT, int D, bool CAUSAL>
-Launch simple_launch() {
-  return {reinterpret_cast<const void *>(&fa::fa_fwd_kernel<DT, D, CAUSAL>),
-          fa::Cfg<DT, D, CAUSAL>::LDS_BYTES, fa::Cfg<DT, D, CAUSAL>::BM, 256};
-}
-
-template <int DT, int D, bool CAUSAL>
-Launch pingpong_launch() {
-  return {reinterpret_cast<const void *>(&fa::fa_fwd_pingpong_kernel<DT, D, CAUSAL>),
-          fa::PPCfg<DT, D, CAUSAL>::LDS_BYTES, fa::PPCfg<DT, D, CAUSAL>::BM, 512};
-}
-
-template <int DT, int D, bool CAUSAL>
-Launch interleaved_launch() {
-  return {reinterpret_cast<const void *>(&fa::fa_fwd_interleaved_kernel<DT, D, CAUSAL>),
-          fa::IWCfg<DT, D, CAUSAL>::LDS_BYTES, fa::IWCfg<DT, D, CAUSAL>::BM, 256};
-}
-
-template <int DT, int D>
-Launch pick_dt_d(int family, int causal) {
-  if constexpr (DT != fa::DT_FP32) {
-    if (family == kPingPong)
-      return causal ? pingpong_launch<DT, D, true>() : pingpong_launch<DT, D, false>();
-    if (family == kInterleaved)
-      return causal ? interleaved_launch<DT, D, true>() : interleaved_launch<DT, D, false>();
-  }
-  return causal ? simple_launch<DT, D, true>() : simple_launch<DT, D, false>();
-}
-
-bool pick(int dtype, int64_t D, int causal, int family, Launch *out) {
+bool pick(int dtype, int64_t D, int causal, int family, FaLaunch *out) {
   if (family == -1) family = kSimple;
-  if (family != kSimple && dtype == FA_DTYPE_FP32) return false;
-  switch (dtype) {
-    case FA_DTYPE_BF16:
-      if (D == 64) { *out = pick_dt_d<fa::DT_BF16, 64>(family, causal); return true; }
-      if (D == 128) { *out = pick_dt_d<fa::DT_BF16, 128>(family, causal); return true; }
-      return false;
-    case FA_DTYPE_FP16:
-      if (D == 64) { *out = pick_dt_d<fa::DT_FP16, 64>(family, causal); return true; }
-      if (D == 128) { *out = pick_dt_d<fa::DT_FP16, 128>(family, causal); return true; }
-      return false;
-    case FA_DTYPE_FP32:
-      if (D == 64) { *out = pick_dt_d<fa::DT_FP32, 64>(family, causal); return true; }
-      if (D == 128) { *out = pick_dt_d<fa::DT_FP32, 128>(family, causal); return true; }
-      return false;
-    default:
-      return false;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return false;
+  if (D != 64 && D != 128) return false;
+  switch (family) {
+    case kSimple:
+      *out = dtype == FA_DTYPE_FP32   ? fa_simple_instance_fp32((int)D, causal != 0)
+             : dtype == FA_DTYPE_FP16 ? fa_simple_instance_fp16((int)D, causal != 0)
+                                      : fa_simple_instance_bf16((int)D, causal != 0);
+      break;
+    case kPingPong: *out = fa_pingpong_instance(dtype, (int)D, causal != 0); break;
+    case kInterleaved: *out = fa_interleaved_instance(dtype, (int)D, causal != 0); break;
+    default: return false;
   }
+  return out->fn != nullptr;
 }
 
 int elem_bytes(int dtype) {
@@ -147,7 +106,7 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   int rc = validate(q, k, v, o, lse, B, H, N, n_kv, D, scale, dtype);
   if (rc != FA_OK) return rc;
   if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
-  Launch L;
+  FaLaunch L;
   if (!pick(dtype, D, causal, kVariants[variant].family, &L)) return FA_ERR_UNSUPPORTED;
   if (L.lds > 65536) opt_in_lds(L.fn, L.lds);
 

@@ -10,35 +10,41 @@
 // 512 registers each) and 128 query rows. Iteration j of a wave runs
 //
 //   a stream of MFMA "slots": PV(j-1) then QK(j+1)   (matrix core)
-//   the softmax of tile j, cut into short chunks    (vector ALU)
+//   the softmax of tile j, cut into short units      (vector ALU)
 //
-// with one softmax chunk and the LDS reads of a later slot placed between
-// consecutive MFMAs, so the vector work and the LDS latency hide under the
-// MFMAs. The two products never depend on the softmax of the same
-// iteration: S_{j+1} and P_j live in a second register buffer (the loop is
-// unrolled by two to swap them). The accumulator rescale, when the exponent
-// reference moves, waits for PV(j-1) and is applied after the stream.
+// with the softmax units placed between consecutive MFMAs in proportion to
+// their issue cost, and the LDS reads of each slot issued several slots
+// ahead, so the vector work and the LDS latency hide under the MFMAs. The two
+// products never depend on the softmax of the same iteration: S_{j+1} and P_j
+// live in a second register buffer. The accumulator rescale, when the
+// exponent reference moves, waits for PV(j-1) and is applied after the stream.
 //
 // Tiles outside the valid range, or in a wave's causal future, are still
 // multiplied: their keys are masked to -inf, so P is 0 and PV adds zeros.
+// This includes up to three tiles past the end, which round the tile count up
+// to the unroll factor of the main loop.
 // K_{j+1} and V_{j-1} form the LDS stage of iteration j; stages stream
-// through a ring of three buffers, two iterations ahead.
+// through a ring of four buffers, three iterations ahead. The main loop is
+// unrolled by four so that every buffer index, and with it every LDS address
+// offset, is a compile-time constant.
 #pragma once
 
 #include "fa_kernel.hpp"
 
 namespace fa {
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int NWAVES>
 struct IWCfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = NWAVES;
   static constexpr int BM = WAVES * 32;
   static constexpr int BN = 64;
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;
-  static constexpr int STAGES = 3;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // K_{s+1}, then V_{s-1}
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int STAGES = 4;
+  // K tiles of the four stages first, then their V tiles: every fragment
+  // read is a per-lane base register plus an immediate below 64 KB
+  static constexpr int V_REGION = STAGES * TILE_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGES * TILE_BYTES;
   static constexpr int LOADS = TILE_BYTES / (WAVES * 64 * 16);   // per thread per matrix
   static_assert(TILE_BYTES % (WAVES * 64 * 16) == 0, "tile must split into 16-byte lane loads");
 };
@@ -49,18 +55,62 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
+// Softmax work of one tile (NV scores per lane), as a sequence of units:
+//   [0, NV/2)        running max, one 3-input maximum (two scores) per unit
+//   NV/2             combine the chains, swap halves, rescale decision
+//   then NV/2 times  exp2 of two scores (FMA, exp, add each) and their pack
+// with the approximate VALU issue cycles of each unit, so that the units can
+// be spread evenly over the MFMA slots of an iteration.
+template <int NV>
+struct IWUnits {
+  static constexpr int DEC = NV / 2;
+  static constexpr int EXP0 = DEC + 1;
+  static constexpr int TOTAL = EXP0 + (NV / 2) * 3;
+  static constexpr int cost(int u) {
+    return u < DEC ? 4 : u == DEC ? 48 : ((u - EXP0) % 3 == 2 ? 4 : 16);
+  }
+  static constexpr int cum(int u) {
+    int s = 0;
+    for (int i = 0; i < u; ++i) s += cost(i);
+    return s;
+  }
+  // first unit of slot i (of ns): the first unit whose cost starts at or
+  // after the slot's even share of the total
+  static constexpr int begin(int i, int ns) {
+    int u = 0;
+    while (u < TOTAL && cum(u) * ns < cum(TOTAL) * i) ++u;
+    return u;
+  }
+};
+
+// Calls f(std::integral_constant<int, i>) for i = B .. E-1, so that every
+// index in f's body is a compile-time constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ float maxnum3(float a, float b, float c) {
+  // NaN-propagating maximum (v_maximum3_f32): no canonicalisation needed
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+template <int DT, int D, bool CAUSAL, int NWAVES>
+__global__ void __launch_bounds__(NWAVES * 64, 1) fa_fwd_interleaved_kernel(Params p) {
   static_assert(DT == DT_BF16 || DT == DT_FP16, "16-bit inputs only");
-  using C = IWCfg<DT, D, CAUSAL>;
+  using C = IWCfg<DT, D, CAUSAL, NWAVES>;
   constexpr int BN = C::BN, BM = C::BM, RB = C::ROW_BYTES;
   constexpr int NKC = D / 16, NKB = BN / 32, NDB = D / 32, NPC = BN / 16;
   constexpr int NPV = NPC * NDB;            // PV slots
   constexpr int NQK = NKC * NKB;            // QK slots
   constexpr int NS = NPV + NQK;             // MFMA slots per iteration
   constexpr int NV = NKB * 16;              // scores per lane per tile
-  constexpr int kAhead = 6;                 // LDS reads run this many slots ahead
+  constexpr int kAhead = 4;                 // LDS reads run this many slots ahead
   constexpr int PER_STAGE = 2 * C::LOADS;   // LDS-direct loads per thread per stage
+  using U = IWUnits<NV>;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -107,26 +157,32 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // ---- stages: stage s holds K_{s+1} and V_{s-1}, in ring buffer (s+1) % 3 ----
-  const i32x4 k_rsrc = make_rsrc_words(kh, (uint32_t)((int64_t)n_kv * D * 2));
-  const i32x4 v_rsrc = make_rsrc_words(vh, (uint32_t)((int64_t)n_kv * D * 2));
+  // ---- stages: stage s holds K_{s+1} and V_{s-1}, in ring slot (s+1) % 4 ----
+  // A tile's loads use a buffer resource based at its first row whose range
+  // ends at key n_kv (empty for tiles outside [0, n_tiles)), so each thread's
+  // offsets are the same for every tile and rows past the keys read as zeros.
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
-  auto stage_offset = [&](int s) __attribute__((always_inline)) { return (uint32_t)(((s + 1) % C::STAGES) * C::STAGE_BYTES); };
-  auto issue_stage = [&](int s) __attribute__((always_inline)) {
-    const uint32_t kl = smem_base + stage_offset(s);
-    const uint32_t vl = kl + C::TILE_BYTES;
-    const int kt = s + 1, vt = s - 1;
+  uint32_t dma_off[C::LOADS];
+#pragma unroll
+  for (int u = 0; u < C::LOADS; ++u) {
+    const int lds_off = (wave * C::LOADS + u) * 1024 + lane * 16;
+    const int row = lds_off / RB;
+    dma_off[u] = (uint32_t)row * RB + (((lds_off % RB) / 16) ^ swz<RB>(row)) * 16;
+  }
+  auto tile_rsrc = [&](const char *base, int t) __attribute__((always_inline)) {
+    const bool ok = t >= 0 && t < n_tiles;
+    const int start = ok ? t * BN : 0;
+    return make_rsrc_words(base + (int64_t)start * RB, ok ? (uint32_t)(n_kv - start) * RB : 0u);
+  };
+  auto issue_stage = [&](int s, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    const i32x4 kr = tile_rsrc(kh, s + 1);
+    const i32x4 vr = tile_rsrc(vh, s - 1);
 #pragma unroll
     for (int u = 0; u < C::LOADS; ++u) {
-      const int inst = wave * C::LOADS + u;
-      const int lds_off = inst * 1024 + lane * 16;
-      const int row = lds_off / RB;
-      const int lchunk = ((lds_off % RB) / 16) ^ swz<RB>(row);
-      // tiles outside [0, n_tiles) read beyond the resource: zeros
-      const uint32_t koff = (kt >= 0 && kt < n_tiles) ? (uint32_t)(kt * BN + row) * RB + lchunk * 16 : 0xFFFFFF00u;
-      const uint32_t voff = (vt >= 0 && vt < n_tiles) ? (uint32_t)(vt * BN + row) * RB + lchunk * 16 : 0xFFFFFF00u;
-      lds_dma16(k_rsrc, koff, kl + inst * 1024);
-      lds_dma16(v_rsrc, voff, vl + inst * 1024);
+      const uint32_t lds = smem_base + buf * C::TILE_BYTES + (wave * C::LOADS + u) * 1024;
+      lds_dma16(kr, dma_off[u], lds);
+      lds_dma16(vr, dma_off[u], lds + C::V_REGION);
     }
   };
 
@@ -146,16 +202,32 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) koff[kc] = l32 * RB + (((kc * 2 + half) ^ swz<RB>(l32)) * 16);
   }
-  // fragment of slot i: V^T (pc, db) for i < NPV, else K (kc, kb)
-  auto frag = [&](uint32_t st, int slot) __attribute__((always_inline)) -> u32x4 {
-    const char *kl = smem + st;
-    const char *vl = kl + C::TILE_BYTES;
+  // Absolute LDS addresses of the fragments in ring slot 0. They are made
+  // opaque to the compiler so that the slot, key-chunk and region offsets
+  // (all below 64 KB) stay in the instructions' immediate offset field
+  // instead of being re-added to the lane address before every read.
+  uint32_t kaddr[NKC], vaddr[2][NDB];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    kaddr[kc] = smem_base + koff[kc];
+    asm volatile("" : "+v"(kaddr[kc]));
+  }
+#pragma unroll
+  for (int jg = 0; jg < 2; ++jg)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      vaddr[jg][db] = smem_base + C::V_REGION + voff[jg][db];
+      asm volatile("" : "+v"(vaddr[jg][db]));
+    }
+  // fragment of slot i in buffer buf: V^T (pc, db) for i < NPV, else K (kc, kb)
+  auto frag = [&](auto buf_c, int slot) __attribute__((always_inline)) -> u32x4 {
+    constexpr int buf = decltype(buf_c)::value;
     if (slot < NPV) {
       const int pc = slot / NDB, db = slot % NDB;
       u32x4 a;
 #pragma unroll
       for (int jg = 0; jg < 2; ++jg) {
-        const char *addr = vl + voff[jg][db] + pc * 16 * RB;
+        FA_LDS char *addr = (FA_LDS char *)(uintptr_t)vaddr[jg][db] + (buf * C::TILE_BYTES + pc * 16 * RB);
         const u32x2 xx = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)addr));
         a[jg * 2] = xx[0];
         a[jg * 2 + 1] = xx[1];
@@ -163,7 +235,7 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
       return a;
     }
     const int kc = (slot - NPV) / NKB, kb = (slot - NPV) % NKB;
-    return *(const FA_LDS u32x4 *)(kl + koff[kc] + kb * 32 * RB);
+    return *(const FA_LDS u32x4 *)((FA_LDS char *)(uintptr_t)kaddr[kc] + (buf * C::TILE_BYTES + kb * 32 * RB));
   };
 
   f32x16 acc[NDB];
@@ -187,15 +259,15 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
   };
 
   // QK of one tile as a plain pipelined stream (prologue)
-  auto qk_only = [&](uint32_t st, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
-    u32x4 buf[kAhead];
+  auto qk_only = [&](auto buf_c, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+    u32x4 fb[kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) buf[i] = frag(st, NPV + i);
+    for (int i = 0; i < kAhead; ++i) fb[i] = frag(buf_c, NPV + i);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const u32x4 a = buf[i % kAhead];
-      if (i + kAhead < NQK) buf[i % kAhead] = frag(st, NPV + i + kAhead);
+      const u32x4 a = fb[i % kAhead];
+      if (i + kAhead < NQK) fb[i % kAhead] = frag(buf_c, NPV + i + kAhead);
       const int kc = i / NKB, kb = i % NKB;
       const u32x4 b = {qf[kc][0], qf[kc][1], qf[kc][2], qf[kc][3]};
       s[kb] = mfma16(a, b, kc == 0 ? f32x16{} : s[kb]);
@@ -203,94 +275,106 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(0);
   };
   // PV of one tile as a plain pipelined stream (epilogue)
-  auto pv_only = [&](uint32_t st, const u32x4 (&pp)[NPC]) __attribute__((always_inline)) {
-    u32x4 buf[kAhead];
+  auto pv_only = [&](auto buf_c, const u32x4 (&pp)[NPC]) __attribute__((always_inline)) {
+    u32x4 fb[kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) buf[i] = frag(st, i);
+    for (int i = 0; i < kAhead; ++i) fb[i] = frag(buf_c, i);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const u32x4 a = buf[i % kAhead];
-      if (i + kAhead < NPV) buf[i % kAhead] = frag(st, i + kAhead);
+      const u32x4 a = fb[i % kAhead];
+      if (i + kAhead < NPV) fb[i % kAhead] = frag(buf_c, i + kAhead);
       acc[i % NDB] = mfma16(a, pp[i / NDB], acc[i % NDB]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // masks of tile t on its scores (only tiles past the keys or on the diagonal)
+  // Score i of block kb is key kstart + half*4 + off(kb, i) with the
+  // compile-time off = kb*32 + 8*(i/4) + i%4; it is masked when off reaches
+  // lim, the first invisible key (past n_kv, or past this row's diagonal)
+  // relative to kstart + half*4.
   auto mask_tile = [&](int t, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
     const int kstart = t * BN;
-    if ((kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw)) {
+    if ((kstart + BN > kend) || (CAUSAL && kstart + BN - 1 > qw)) {
+      int lim = n_kv - kstart - half * 4;
+      if (CAUSAL) lim = min(lim, my_q + 1 - kstart - half * 4);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kstart + kb * 32 + 8 * (i / 4) + half * 4 + (i % 4);
-          if ((key >= n_kv) || (CAUSAL && key > my_q)) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i / 4) + (i % 4) >= lim) s[kb][i] = -INFINITY;
     }
   };
 
-  // ---- one iteration: softmax(j) on sc -> pc_out, MFMAs PV(j-1) with pp and QK(j+1) into sn ----
-  // Softmax work is cut into units spread evenly over the NS slots:
-  //   [0, NV/2)           running max, two scores per unit (two chains)
-  //   NV/2                new reference, rescale decision
-  //   NV/2+1 ... +NV      exp2 and row sum, one score per unit
-  //   then NPC*4 units    pack two probabilities into one 16-bit pair
-  constexpr int U_MAX0 = 0, U_DEC = NV / 2, U_EXP0 = U_DEC + 1, U_PACK0 = U_EXP0 + NV;
-  constexpr int U_TOTAL = U_PACK0 + NPC * 4;
-  auto iteration = [&](int j, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4 (&pp)[NPC],
+  // ---- one iteration (phase ph = j % 4): softmax(j) on sc -> po,
+  //      MFMAs PV(j-1) with pp and QK(j+1) into sn ----
+  auto iteration = [&](int j, auto ph_c, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], const u32x4 (&pp)[NPC],
                        u32x4 (&po)[NPC]) __attribute__((always_inline)) {
-    const uint32_t st = stage_offset(j);
+    constexpr int ph = decltype(ph_c)::value;
+    constexpr int buf = (ph + 1) % 4;          // stage j lives in buffer (j+1) % 4
+    const auto bufc = std::integral_constant<int, buf>{};
+
+    issue_stage(j + 3, std::integral_constant<int, ph>{});   // buffer (j+4) % 4
     mask_tile(j, sc);
     float mx0 = -INFINITY, mx1 = -INFINITY, rs0 = 0.f, rs1 = 0.f, neg = 0.f, alpha = 1.f;
     bool rescale = false;
-    auto unit = [&](int u) __attribute__((always_inline)) {
-      if (u < U_DEC) {
+    auto unit = [&](auto u_c) __attribute__((always_inline)) {
+      constexpr int u = decltype(u_c)::value;
+      if constexpr (u < U::DEC) {
         const int e = 2 * u;
         const float x0 = sc[e / 16][e % 16], x1 = sc[(e + 1) / 16][(e + 1) % 16];
-        if (u & 1) mx1 = fmaxf(mx1, fmaxf(x0, x1));
-        else mx0 = fmaxf(mx0, fmaxf(x0, x1));
-      } else if (u == U_DEC) {
-        const float mx = halves_max(fmaxf(mx0, mx1)) * c;
+        if constexpr (u & 1) mx1 = maxnum3(mx1, x0, x1);
+        else mx0 = maxnum3(mx0, x0, x1);
+      } else if constexpr (u == U::DEC) {
+        const float m2 = __builtin_elementwise_maximum(mx0, mx1);
+        const u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
+            __float_as_uint(m2), __float_as_uint(m2), false, false));
+        const float mx = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])) * c;
         rescale = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0;
-        if (rescale) {
-          const float m_new = fmaxf(m_run, mx);
-          alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-        }
+        const float m_new = rescale ? __builtin_elementwise_maximum(m_run, mx) : m_run;
+        // alpha = 0 on the first visible tile (m_run = -inf), 1 if unchanged
+        alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
         neg = (m_run == -INFINITY) ? 0.f : -m_run;
-      } else if (u < U_PACK0) {
-        const int e = u - U_EXP0;
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / 16][e % 16], c, neg));
-        sc[e / 16][e % 16] = x;
-        if (e & 1) rs1 += x;
-        else rs0 += x;
-      } else if (u < U_TOTAL) {
-        const int k = u - U_PACK0;
-        const int pc = k / 4, w = k % 4, kb = pc / 2, i0 = (pc % 2) * 8 + 2 * w;
-        po[pc][w] = pack2<DT>(sc[kb][i0], sc[kb][i0 + 1]);
+      } else {
+        constexpr int k = (u - U::EXP0) / 3, part = (u - U::EXP0) % 3;
+        constexpr int pc = k / 4, w = k % 4, kb = pc / 2, i0 = (pc % 2) * 8 + 2 * w;
+        if constexpr (part < 2) {
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i0 + part], c, neg));
+          sc[kb][i0 + part] = x;
+          if constexpr (part) rs1 += x;
+          else rs0 += x;
+        } else {
+          po[pc][w] = pack2<DT>(sc[kb][i0], sc[kb][i0 + 1]);
+        }
       }
     };
-    u32x4 buf[kAhead];
+    u32x4 fb[kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) buf[i] = frag(st, i);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < kAhead; ++i) fb[i] = frag(bufc, i);
+    static_for<0, NS>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
       __builtin_amdgcn_sched_barrier(0);
-      const u32x4 a = buf[i % kAhead];
-      if (i + kAhead < NS) buf[i % kAhead] = frag(st, i + kAhead);
-      if (i < NPV) {
+      const u32x4 a = fb[i % kAhead];
+      if constexpr (i + kAhead < NS) fb[i % kAhead] = frag(bufc, i + kAhead);
+      if constexpr (i < NPV) {
         acc[i % NDB] = mfma16(a, pp[i / NDB], acc[i % NDB]);
       } else {
-        const int kc = (i - NPV) / NKB, kb = (i - NPV) % NKB;
+        constexpr int kc = (i - NPV) / NKB, kb = (i - NPV) % NKB;
         const u32x4 b = {qf[kc][0], qf[kc][1], qf[kc][2], qf[kc][3]};
         sn[kb] = mfma16(a, b, kc == 0 ? f32x16{} : sn[kb]);
       }
+      static_for<U::begin(i, NS), U::begin(i + 1, NS)>(unit);
+    });
+    // the probabilities are consumed in the next iteration only; pin them
+    // here so that the compiler keeps their computation inside the stream
+    // instead of sinking it past the rescale branch below
 #pragma unroll
-      for (int u = (i * U_TOTAL) / NS; u < ((i + 1) * U_TOTAL) / NS; ++u) unit(u);
-    }
+    for (int pc = 0; pc < NPC; ++pc)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) asm volatile("" : "+v"(po[pc][w]));
     __builtin_amdgcn_sched_barrier(0);
     l_run += rs0 + rs1;
     if (rescale) {
@@ -299,40 +383,33 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_interleaved_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     }
+    wait_vmcnt<2 * PER_STAGE>();          // stage j+1 has landed (j+2, j+3 may be in flight)
+    __syncthreads();
   };
 
-  // ---- prologue: stages -1, 0, 1 in flight; S_0 = QK(0) from stage -1 ----
-  issue_stage(-1);
-  issue_stage(0);
-  issue_stage(1);
+  // ---- prologue: stages -1 .. 2 in flight; S_0 = QK(0) from stage -1 ----
+  issue_stage(-1, std::integral_constant<int, 0>{});
+  issue_stage(0, std::integral_constant<int, 1>{});
+  issue_stage(1, std::integral_constant<int, 2>{});
+  issue_stage(2, std::integral_constant<int, 3>{});
+  wait_vmcnt<3 * PER_STAGE>();
+  __syncthreads();
+  qk_only(std::integral_constant<int, 0>{}, sA);
   wait_vmcnt<2 * PER_STAGE>();
   __syncthreads();
-  qk_only(stage_offset(-1), sA);
-  wait_vmcnt<PER_STAGE>();
-  __syncthreads();
 
-  // ---- main loop, unrolled by two to swap the score / probability buffers ----
-  int j = 0;
-  for (; j + 1 < n_tiles; j += 2) {
-    issue_stage(j + 2);
-    iteration(j, sA, sB, pB, pA);
-    wait_vmcnt<PER_STAGE>();
-    __syncthreads();
-    issue_stage(j + 3);
-    iteration(j + 1, sB, sA, pA, pB);
-    wait_vmcnt<PER_STAGE>();
-    __syncthreads();
+  // ---- main loop, unrolled by four over the tile count rounded up to a
+  //      multiple of four: the extra tiles lie past the visible keys, read as
+  //      zeros and are masked, so they add nothing. The last PV(n-1) reads
+  //      stage n, in slot (n+1) % 4 = 1, with the probabilities of phase 3 ----
+  const int n_pad = (n_tiles + 3) & ~3;
+  for (int j = 0; j < n_pad; j += 4) {
+    iteration(j, std::integral_constant<int, 0>{}, sA, sB, pB, pA);
+    iteration(j + 1, std::integral_constant<int, 1>{}, sB, sA, pA, pB);
+    iteration(j + 2, std::integral_constant<int, 2>{}, sA, sB, pB, pA);
+    iteration(j + 3, std::integral_constant<int, 3>{}, sB, sA, pA, pB);
   }
-  if (j < n_tiles) {
-    // odd tile count: last softmax reads sA, its P goes to pA; PV(n-2) used pB
-    issue_stage(j + 2);
-    iteration(j, sA, sB, pB, pA);
-    wait_vmcnt<PER_STAGE>();
-    __syncthreads();
-    pv_only(stage_offset(n_tiles), pA);
-  } else if (n_tiles > 0) {
-    pv_only(stage_offset(n_tiles), pB);
-  }
+  pv_only(std::integral_constant<int, 1>{}, pB);
   wait_vmcnt<0>();
 
   // ---- finalize ----

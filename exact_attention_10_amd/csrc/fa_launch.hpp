@@ -1,0 +1,20 @@
+// Kernel instance tables shared by the host API and the instance files.
+//
+// Each kernel family is instantiated in a translation unit of its own
+// (fa_inst_*.hip), so the instances compile in parallel; the host API picks
+// an instance through these functions.
+#pragma once
+
+struct FaLaunch {
+  const void *fn;   // __global__ function, nullptr if the combination has no instance
+  int lds;          // dynamic LDS bytes per workgroup
+  int bm;           // query rows per workgroup
+  int threads;      // threads per workgroup
+};
+
+// dt: 0 fp32, 1 fp16, 2 bf16 (the values of the fa.h dtype codes); d: 64 or 128
+FaLaunch fa_simple_instance_fp32(int d, bool causal);
+FaLaunch fa_simple_instance_fp16(int d, bool causal);
+FaLaunch fa_simple_instance_bf16(int d, bool causal);
+FaLaunch fa_pingpong_instance(int dt, int d, bool causal);
+FaLaunch fa_interleaved_instance(int dt, int d, bool causal);

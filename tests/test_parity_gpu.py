@@ -74,7 +74,7 @@ def test_key_length_mask(dtype, causal, n_kv):
         assert (o == 0).all() and np.isneginf(lse).all()
 
 
-@pytest.mark.parametrize("variant", range(8))
+@pytest.mark.parametrize("variant", range(16))
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64), ("fp32", 64)])
 def test_variants(variant, causal, dtype, D):
