@@ -20,36 +20,46 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
-enum Family { kSimple = 0, kPingPong = 1, kInterleaved = 2 };
+enum Family { kDefault = -1, kSimple = 0, kPingPong = 1, kInterleaved = 2 };
 
 struct Variant {
   const char *name;
-  int family;      // kernel family; 16-bit inputs only for kPingPong
+  int family;      // kernel family; 16-bit inputs only for kPingPong and kInterleaved
+  int waves;       // waves per workgroup of the simple family (0 = per-shape default)
   int xcd_remap;
 };
 
-// Variants of the same computation; 0 is what fa_fwd runs (the fastest
-// measured family for every dtype).
+// Variants of the same computation; 0 is what fa_fwd runs.
 const Variant kVariants[] = {
-    {"default", -1, 1},
-    {"simple_bm128_xcd", kSimple, 1},
-    {"simple_bm128_linear", kSimple, 0},
-    {"pingpong_bm256_xcd", kPingPong, 1},
-    {"pingpong_bm256_linear", kPingPong, 0},
-    {"interleaved_bm128_xcd", kInterleaved, 1},
-    {"interleaved_bm128_linear", kInterleaved, 0},
+    {"default", kDefault, 0, 1},
+    {"simple_bm128_xcd", kSimple, 4, 1},
+    {"simple_bm128_linear", kSimple, 4, 0},
+    {"pingpong_bm256_xcd", kPingPong, 0, 1},
+    {"pingpong_bm256_linear", kPingPong, 0, 0},
+    {"interleaved_bm128_xcd", kInterleaved, 0, 1},
+    {"interleaved_bm128_linear", kInterleaved, 0, 0},
+    {"simple_bm256_xcd", kSimple, 8, 1},
+    {"simple_bm256_linear", kSimple, 8, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-bool pick(int dtype, int64_t D, int causal, int family, FaLaunch *out) {
-  if (family == -1) family = kSimple;
+// The default is the simple family; 16-bit non-causal D=128 runs it with 8
+// waves (256 query rows share each K/V tile), which measured fastest there,
+// and every other shape with 4.
+int default_waves(int dtype, int64_t D, int causal) {
+  return (dtype != FA_DTYPE_FP32 && D == 128 && !causal) ? 8 : 4;
+}
+
+bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return false;
   if (D != 64 && D != 128) return false;
-  switch (family) {
+  const int waves = var.waves ? var.waves : default_waves(dtype, D, causal);
+  switch (var.family) {
+    case kDefault:
     case kSimple:
-      *out = dtype == FA_DTYPE_FP32   ? fa_simple_instance_fp32((int)D, causal != 0)
-             : dtype == FA_DTYPE_FP16 ? fa_simple_instance_fp16((int)D, causal != 0)
-                                      : fa_simple_instance_bf16((int)D, causal != 0);
+      *out = dtype == FA_DTYPE_FP32   ? fa_simple_instance_fp32((int)D, causal != 0, waves)
+             : dtype == FA_DTYPE_FP16 ? fa_simple_instance_fp16((int)D, causal != 0, waves)
+                                      : fa_simple_instance_bf16((int)D, causal != 0, waves);
       break;
     case kPingPong: *out = fa_pingpong_instance(dtype, (int)D, causal != 0); break;
     case kInterleaved: *out = fa_interleaved_instance(dtype, (int)D, causal != 0); break;
@@ -107,7 +117,7 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   if (rc != FA_OK) return rc;
   if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
   FaLaunch L;
-  if (!pick(dtype, D, causal, kVariants[variant].family, &L)) return FA_ERR_UNSUPPORTED;
+  if (!pick(dtype, D, causal, kVariants[variant], &L)) return FA_ERR_UNSUPPORTED;
   if (L.lds > 65536) opt_in_lds(L.fn, L.lds);
 
   fa::Params p;

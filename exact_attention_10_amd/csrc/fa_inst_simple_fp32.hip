@@ -1,5 +1,5 @@
 // Instances of the default kernel (fa_kernel.hpp) for fp32 inputs: D in {64, 128},
-// both masks. One translation unit per dtype so the instances compile in parallel.
+// both masks, 4 waves per workgroup. One translation unit per dtype so the instances compile in parallel.
 #include "fa_kernel.hpp"
 #include "fa_launch.hpp"
 
@@ -11,7 +11,8 @@ FaLaunch make() {
 }
 }  // namespace
 
-FaLaunch fa_simple_instance_fp32(int d, bool causal) {
+FaLaunch fa_simple_instance_fp32(int d, bool causal, int waves) {
+  if (waves != 4) return {nullptr, 0, 0, 0};
   if (d == 64) return causal ? make<64, true>() : make<64, false>();
   if (d == 128) return causal ? make<128, true>() : make<128, false>();
   return {nullptr, 0, 0, 0};

@@ -1,7 +1,7 @@
 // FlashAttention-2 forward kernel for gfx950 (CDNA4), hand-written HIP.
 //
-// One workgroup owns one (batch*head, query tile) pair: 4 waves, 32 query rows
-// per wave, 128 rows per tile. The workgroup streams the head's key/value tiles
+// One workgroup owns one (batch*head, query tile) pair: 4 or 8 waves, 32 query
+// rows per wave, 128 or 256 rows per tile. The workgroup streams the head's key/value tiles
 // (64 keys each) through LDS, double-buffered, with direct global->LDS buffer
 // loads; each wave keeps the online-softmax state of its 32 rows in registers
 // and never writes a score to memory ("A09 - Advanced Triton &
@@ -152,9 +152,9 @@ __device__ __forceinline__ int swz(int r) {
 // ---------------------------------------------------------------------------
 // The kernel
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int WAVES_ = 4>
 struct Cfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = WAVES_;      // 4 or 8 (two per SIMD with 8)
   static constexpr int BM = WAVES * 32;     // query rows per workgroup
   static constexpr int BN = 64;             // keys per tile
   static constexpr int ES = Elem<DT>::bytes;
@@ -166,10 +166,13 @@ struct Cfg {
 };
 
 // Register budget: two waves per SIMD (256 VGPRs) for 16-bit inputs, one wave
-// per SIMD for fp32, whose Q fragments are twice as wide.
-template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Params p) {
-  using C = Cfg<DT, D, CAUSAL>;
+// per SIMD for fp32, whose Q fragments are twice as wide. With 8 waves the
+// workgroup holds both waves of every SIMD and shares each K/V tile between
+// 256 query rows, halving the global->LDS traffic per query row.
+template <int DT, int D, bool CAUSAL, int WAVES = 4>
+__global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Params p) {
+  static_assert(WAVES == 4 || (WAVES == 8 && DT != DT_FP32), "4 waves, or 8 for 16-bit inputs");
+  using C = Cfg<DT, D, CAUSAL, WAVES>;
   constexpr int ES = C::ES, BN = C::BN, BM = C::BM, RB = C::ROW_BYTES;
   constexpr int KSTEP = Elem<DT>::k_step;
   constexpr int NKC = D / KSTEP;           // MFMAs along the head dim for S^T
@@ -414,16 +417,18 @@ __global__ void __launch_bounds__(256, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Pa
     }
     // a row that has seen no visible key has only -inf scores: p = 0
     const float neg = (m_run == -INFINITY) ? 0.f : -m_run;
-    float rs = 0.f;
+    // row sum in four interleaved partial sums (short dependency chains)
+    float rs[4];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, neg));
         s[kb][i] = e;
-        rs += e;
+        if (kb == 0 && i < 4) rs[i] = e;
+        else rs[i % 4] += e;
       }
-    l_run += rs;
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
     // ---- O^T += V^T P^T ----
     if constexpr (DT == DT_FP32) {

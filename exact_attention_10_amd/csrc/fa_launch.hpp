@@ -13,8 +13,9 @@ struct FaLaunch {
 };
 
 // dt: 0 fp32, 1 fp16, 2 bf16 (the values of the fa.h dtype codes); d: 64 or 128
-FaLaunch fa_simple_instance_fp32(int d, bool causal);
-FaLaunch fa_simple_instance_fp16(int d, bool causal);
-FaLaunch fa_simple_instance_bf16(int d, bool causal);
+// waves: 4 or 8 per workgroup (8 for 16-bit dtypes only)
+FaLaunch fa_simple_instance_fp32(int d, bool causal, int waves);
+FaLaunch fa_simple_instance_fp16(int d, bool causal, int waves);
+FaLaunch fa_simple_instance_bf16(int d, bool causal, int waves);
 FaLaunch fa_pingpong_instance(int dt, int d, bool causal);
 FaLaunch fa_interleaved_instance(int dt, int d, bool causal);

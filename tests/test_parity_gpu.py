@@ -76,14 +76,14 @@ def test_key_length_mask(dtype, causal, n_kv):
 
 @pytest.mark.parametrize("variant", range(16))
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 128), ("fp16", 64), ("fp32", 64)])
 def test_variants(variant, causal, dtype, D):
     """Every kernel variant (tile shape / schedule / workgroup order) computes
     the same attention; variants that only reorder workgroups agree bitwise."""
     if variant >= fa.fa_num_variants():
         pytest.skip("no such variant")
     name = fa.fa_variant_name(variant)
-    if dtype == "fp32" and name != "default" and not name.startswith("simple"):
+    if dtype == "fp32" and name != "default" and not name.startswith("simple_bm128"):
         pytest.skip("schedule for 16-bit inputs only")
     _banner(f"variant {variant} ({name}) dtype={dtype} D={D} causal={causal}")
     B, H, N = 2, 4, 520
