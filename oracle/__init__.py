@@ -54,8 +54,8 @@ def load(path: str = LIBRARY):
     lib = ctypes.CDLL(path)
     fn = lib.oracle_attention_rows
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 4 + [
-        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+    fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p]
     _lib_cache[path] = lib
     return lib
@@ -70,41 +70,59 @@ def _as_bhnd(x):
     raise ValueError("expected [BH, N, D] or [B, H, N, D]")
 
 
-def attention_rows(q, k, v, scale, causal, rows, n_kv=None, lib_path=LIBRARY):
+ALIGNMENTS = ("top-left", "bottom-right")
+
+
+def causal_offset(nq, nk, causal_align):
+    """The diagonal shift coff of the causal mask (query i sees keys j <= i + coff):
+    0 for the top-left alignment, Nk - Nq for the bottom-right one."""
+    if causal_align not in ALIGNMENTS:
+        raise ValueError(f"causal_align must be one of {ALIGNMENTS}")
+    return 0 if causal_align == "top-left" else nk - nq
+
+
+def attention_rows(q, k, v, scale, causal, rows, n_kv=None, causal_align="top-left",
+                   lib_path=LIBRARY):
     """O and LSE for the listed rows.
 
-    q, k, v: float32 arrays [B, H, N, D] or [BH, N, D] holding exact input
-    values. rows: int array of shape [R, 2] with (flattened head bh, query i).
-    n_kv: keys >= n_kv are masked (default N). Returns (o [R, D], lse [R]) fp64.
+    q: float32 array [B, H, Nq, D] or [BH, Nq, D]; k, v: [.., Nk, D], holding
+    exact input values. rows: int array of shape [R, 2] with (flattened head
+    bh, query i). n_kv: keys >= n_kv are masked (default Nk). causal_align:
+    "top-left" or "bottom-right" (only used when causal). Returns
+    (o [R, D], lse [R]) in fp64.
     """
     q3, k3, v3 = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v)
-    BH, N, D = q3.shape
-    if k3.shape != q3.shape or v3.shape != q3.shape:
-        raise ValueError("q, k, v must have the same shape")
+    BH, Nq, D = q3.shape
+    Nk = k3.shape[1]
+    if k3.shape != (BH, Nk, D) or v3.shape != k3.shape:
+        raise ValueError("k and v must be [BH, Nk, D] with the heads and D of q")
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
     R = rows.shape[0]
     o = np.empty((R, D), dtype=np.float64)
     lse = np.empty((R,), dtype=np.float64)
     if n_kv is None:
-        n_kv = N
+        n_kv = Nk
+    coff = causal_offset(Nq, Nk, causal_align)
     rc = load(lib_path).oracle_attention_rows(
-        q3.ctypes.data, k3.ctypes.data, v3.ctypes.data, BH, N, int(n_kv), D,
-        float(scale), int(bool(causal)), rows.ctypes.data, R,
+        q3.ctypes.data, k3.ctypes.data, v3.ctypes.data, BH, Nq, Nk, int(n_kv), D,
+        float(scale), int(bool(causal)), int(coff), rows.ctypes.data, R,
         o.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_attention_rows failed with code {rc}")
     return o, lse
 
 
-def attention(q, k, v, scale, causal, n_kv=None, lib_path=LIBRARY):
-    """O [..., N, D] and LSE [..., N] for every row (small inputs only)."""
+def attention(q, k, v, scale, causal, n_kv=None, causal_align="top-left", lib_path=LIBRARY):
+    """O [..., Nq, D] and LSE [..., Nq] for every row (small inputs only)."""
     q = np.asarray(q)
+    k = np.asarray(k)
     lead = q.shape[:-2]
-    N, D = q.shape[-2:]
+    Nq, D = q.shape[-2:]
+    Nk = k.shape[-2]
     BH = int(np.prod(lead)) if lead else 1
-    bh, i = np.meshgrid(np.arange(BH), np.arange(N), indexing="ij")
+    bh, i = np.meshgrid(np.arange(BH), np.arange(Nq), indexing="ij")
     rows = np.stack([bh.ravel(), i.ravel()], axis=1)
-    o, lse = attention_rows(q.reshape(BH, N, D), np.asarray(k).reshape(BH, N, D),
-                            np.asarray(v).reshape(BH, N, D), scale, causal, rows,
-                            n_kv, lib_path)
-    return o.reshape(*lead, N, D), lse.reshape(*lead, N)
+    o, lse = attention_rows(q.reshape(BH, Nq, D), k.reshape(BH, Nk, D),
+                            np.asarray(v).reshape(BH, Nk, D), scale, causal, rows,
+                            n_kv, causal_align, lib_path)
+    return o.reshape(*lead, Nq, D), lse.reshape(*lead, Nq)

@@ -25,25 +25,26 @@ def _rand(shape, seed, scale=1.0):
     return (rng.standard_normal(shape) * scale).astype(np.float32)
 
 
-def decimal_attention(q, k, v, scale, causal, n_kv=None, prec=60):
+def decimal_attention(q, k, v, scale, causal, n_kv=None, coff=0, prec=60):
     """Brute force in high-precision decimal straight from the definition:
     O_i = sum_j e^{s_ij} v_j / sum_j e^{s_ij}, LSE_i = ln sum_j e^{s_ij},
-    s_ij = scale * q_i . k_j, over visible keys (j < n_kv, and j <= i if
-    causal). No max subtraction: exact arithmetic does not need it.
-    q, k, v: [N, D] float32. Returns (O, LSE) as float64 arrays.
+    s_ij = scale * q_i . k_j, over visible keys (j < n_kv, and j <= i + coff
+    if causal). No max subtraction: exact arithmetic does not need it.
+    q: [Nq, D], k, v: [Nk, D] float32. Returns (O, LSE) as float64 arrays.
     """
-    N, D = q.shape
-    n_kv = N if n_kv is None else n_kv
-    o = np.zeros((N, D))
-    lse = np.full(N, -np.inf)
+    Nq, D = q.shape
+    Nk = k.shape[0]
+    n_kv = Nk if n_kv is None else n_kv
+    o = np.zeros((Nq, D))
+    lse = np.full(Nq, -np.inf)
     with localcontext() as ctx:
         ctx.prec = prec
         sc = Decimal(float(scale))
         qd = [[Decimal(float(x)) for x in row] for row in q]
         kd = [[Decimal(float(x)) for x in row] for row in k]
         vd = [[Decimal(float(x)) for x in row] for row in v]
-        for i in range(N):
-            vis = [j for j in range(n_kv) if (not causal or j <= i)]
+        for i in range(Nq):
+            vis = [j for j in range(n_kv) if (not causal or j <= i + coff)]
             if not vis:
                 continue
             w = {j: (sc * sum(a * b for a, b in zip(qd[i], kd[j]))).exp() for j in vis}
@@ -59,7 +60,8 @@ def _close(a, b, tol, what):
     b = np.asarray(b, dtype=np.float64)
     assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
     same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    err = np.where(same_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):
+        err = np.where(same_inf, 0.0, np.abs(a - b))
     bound = tol * np.maximum(1.0, np.where(same_inf, 1.0, np.abs(b)))
     bad = ~(err <= bound)
     assert not bad.any(), f"{what}: max err {np.nanmax(np.where(bad, err, 0))}"
@@ -247,9 +249,77 @@ def pin_multi_head_rows(lib_path=oracle.LIBRARY):
         _close(lse[r], lse_ref[i], 1e-13, f"head {bh} row {i} LSE")
 
 
+def pin_cross_attention_brute_force(lib_path=oracle.LIBRARY):
+    """Query and key lengths are separate ("Triton: FlashAttention-2 Forward
+    Pass", Masks and sentinels: Q rows and the output use the query length,
+    the key loop and K/V rows the key length). Several heads, Nq < Nk and
+    Nq > Nk, both causal alignments ("How to profile and optimise kernels",
+    Round 4: top-left as SDPA's is_causal, bottom-right as FlashAttention
+    since 2.1), against the decimal brute force."""
+    BH, D = 2, 3
+    for seed, (nq, nk) in enumerate([(3, 7), (7, 3), (1, 2), (4, 4)]):
+        q = _rand((BH, nq, D), 160 + seed)
+        k = _rand((BH, nk, D), 170 + seed)
+        v = _rand((BH, nk, D), 180 + seed)
+        for causal, align in ((False, "top-left"), (True, "top-left"), (True, "bottom-right")):
+            coff = 0 if align == "top-left" else nk - nq
+            o, lse = oracle.attention(q, k, v, 0.6, causal, causal_align=align,
+                                      lib_path=lib_path)
+            for bh in range(BH):
+                o_ref, lse_ref = decimal_attention(q[bh], k[bh], v[bh], 0.6, causal, coff=coff)
+                what = f"Nq={nq} Nk={nk} causal={causal} {align} head {bh}"
+                _close(o[bh], o_ref, 1e-13, what)
+                _close(lse[bh], lse_ref, 1e-13, what + " LSE")
+
+
+def pin_one_query_two_keys(lib_path=oracle.LIBRARY):
+    """One query, two keys with equal scores (Q = 0) and value rows 5 and 10:
+    O = 7.5 and LSE = ln 2. The pages report a kernel that took the key
+    length from Q returning 5 for a one-query, two-key case ("Triton:
+    FlashAttention-2 Forward Pass", Masks and sentinels); here 5 is what
+    a top-left causal mask gives, since query 0 then sees key 0 only, while
+    the bottom-right alignment (offset Nk - Nq = 1) sees both keys."""
+    D = 4
+    q = np.zeros((1, 1, D), np.float32)
+    k = _rand((1, 2, D), 190)
+    v = np.array([[[5.0] * D, [10.0] * D]], np.float32)
+    for causal, align, o_want, lse_want in (
+            (False, "top-left", 7.5, math.log(2.0)),
+            (True, "bottom-right", 7.5, math.log(2.0)),
+            (True, "top-left", 5.0, 0.0)):
+        o, lse = oracle.attention(q, k, v, 0.5, causal, causal_align=align, lib_path=lib_path)
+        _close(o[0, 0], np.full(D, o_want), 1e-15, f"one query two keys {causal} {align}")
+        _close(lse[0, 0], lse_want, 1e-15, f"one query two keys LSE {causal} {align}")
+
+
+def pin_bottom_right_rows(lib_path=oracle.LIBRARY):
+    """Bottom-right alignment: the last query row sees every key, so it equals
+    the non-causal row; with more queries than keys, the first Nq - Nk rows
+    see no key at all (O = 0, LSE = -inf) and row Nq - Nk sees key 0 only
+    (O = V[0], LSE = scale q.k_0)."""
+    D = 4
+    for nq, nk in ((3, 8), (8, 3)):
+        q = _rand((1, nq, D), 200 + nq)
+        k = _rand((1, nk, D), 210 + nq)
+        v = _rand((1, nk, D), 220 + nq)
+        o_c, l_c = oracle.attention(q, k, v, 0.4, True, causal_align="bottom-right",
+                                    lib_path=lib_path)
+        o_n, l_n = oracle.attention(q, k, v, 0.4, False, lib_path=lib_path)
+        _close(o_c[0, -1], o_n[0, -1], 1e-15, "last row sees every key")
+        _close(l_c[0, -1], l_n[0, -1], 1e-15, "last row LSE")
+        if nq > nk:
+            first = nq - nk
+            assert (o_c[0, :first] == 0).all() and np.isneginf(l_c[0, :first]).all(), \
+                "rows above the shifted diagonal see no key"
+            _close(o_c[0, first], v[0, 0], 0.0, "first visible row is V[0]")
+            s0 = 0.4 * math.fsum(float(a) * float(b) for a, b in zip(q[0, first], k[0, 0]))
+            _close(l_c[0, first], s0, 1e-15, "first visible row LSE")
+
+
 ALL_PINS = [
     pin_decimal_brute_force, pin_scipy_softmax, pin_rows_sum_to_one, pin_single_key,
     pin_constant_values, pin_key_permutation, pin_zero_queries, pin_causal_first_row,
     pin_value_shift, pin_power_of_two_rescale, pin_large_scores, pin_no_visible_key,
-    pin_multi_head_rows,
+    pin_multi_head_rows, pin_cross_attention_brute_force, pin_one_query_two_keys,
+    pin_bottom_right_rows,
 ]

@@ -83,11 +83,15 @@ def test_thread_count_does_not_change_results():
 # check that at least one pin fails on it.
 
 MUTANTS = {
-    "causal_excludes_diagonal": ("if (causal && i + 1 < n_vis) n_vis = i + 1;",
-                                 "if (causal && i < n_vis) n_vis = i;"),
+    "causal_excludes_diagonal": ("if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;",
+                                 "if (causal && i + coff < n_vis) n_vis = i + coff;"),
+    "causal_offset_dropped": ("if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;",
+                              "if (causal && i + 1 < n_vis) n_vis = i + 1;"),
+    "key_count_from_query_length": ("int64_t n_vis = n_kv;",
+                                    "int64_t n_vis = n_kv < Nq ? n_kv : Nq;"),
     "dropped_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
     "transposed_key_operand": ("dot += (double)qi[d] * (double)kj[d];",
-                               "dot += (double)qi[d] * (double)kh[d * N + j];"),
+                               "dot += (double)qi[d] * (double)kh[d * Nk + j];"),
     "exp_sign_flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     "lse_dropped_max": ("lse[r] = m + log(l);", "lse[r] = log(l);"),
     "value_row_index": ("const float *vj = vh + j * D;", "const float *vj = vh + i * D;"),
