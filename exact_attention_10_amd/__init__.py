@@ -8,6 +8,8 @@ library is missing, calls raise ``RuntimeError``.
 The functions mirror the C ABI of ``include/fa.h``:
 
 * :func:`fa_fwd` -- O = softmax(scale * Q K^T) V and the row log-sum-exp;
+* :func:`fa_fwd_ex` -- the same with separate query and key lengths and a
+  top-left or bottom-right causal mask;
 * :func:`fa_fwd_nk` -- the same with only the first ``n_kv`` keys visible;
 * :func:`fa_fwd_variant` -- run a named kernel variant (tuning);
 * :func:`fa_num_variants`, :func:`fa_variant_name`, :func:`fa_strerror`,
@@ -23,12 +25,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libfa_mi355x.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
+FA_CAUSAL_TOP_LEFT, FA_CAUSAL_BOTTOM_RIGHT = 0, 1
+_ALIGN = {"top-left": FA_CAUSAL_TOP_LEFT, "bottom-right": FA_CAUSAL_BOTTOM_RIGHT}
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGNMENT, FA_ERR_HIP = 0, -1, -2, -3, -4
 
 # names and argument types of every exported symbol of include/fa.h
 _P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
+    "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "fa_fwd_nk": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_fwd_variant": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P, _I]),
     "fa_num_variants": (_I, []),
@@ -83,13 +88,15 @@ def _check(code: int):
         raise FAError(code, fa_strerror(code))
 
 
-def _prepare(q, k, v, o, lse, with_lse):
+def _prepare(q, k, v, o, lse, with_lse, same_length=True):
     import torch
-    if q.dim() != 4:
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, D]")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError(f"{name} must match q in shape, dtype and device")
+    kv_shape = q.shape if same_length else (q.shape[0], q.shape[1], k.shape[2], q.shape[3])
+    for name, t, shape in (("q", q, q.shape), ("k", k, kv_shape), ("v", v, kv_shape)):
+        if t.shape != shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device"
+                             + ("" if same_length else " (k and v may differ in N)"))
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     if o is None:
@@ -161,6 +168,28 @@ def fa_fwd(q, k, v, o=None, lse=None, *, causal=False, scale=None, stream=None,
                     lse.data_ptr() if lse is not None else None,
                     B, H, N, D, int(bool(causal)), float(scale), _dtype_code(q),
                     _stream_handle(q, stream))
+    _check(rc)
+    return o, lse
+
+
+def fa_fwd_ex(q, k, v, o=None, lse=None, *, causal=False, causal_align="top-left",
+              scale=None, stream=None, with_lse=True):
+    """Attention with separate query and key lengths: q [B, H, Nq, D], k and v
+    [B, H, Nk, D]; returns (o [B, H, Nq, D], lse [B, H, Nq]). ``causal_align``
+    is "top-left" (query i sees keys j <= i) or "bottom-right"
+    (j <= i + Nk - Nq)."""
+    lib = load_library()
+    if causal_align not in _ALIGN:
+        raise ValueError(f"causal_align must be one of {sorted(_ALIGN)}")
+    o, lse = _prepare(q, k, v, o, lse, with_lse, same_length=False)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = lib.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr() if lse is not None else None,
+                       B, H, Nq, Nk, D, int(bool(causal)), _ALIGN[causal_align], float(scale),
+                       _dtype_code(q), _stream_handle(q, stream))
     _check(rc)
     return o, lse
 

@@ -20,11 +20,11 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
-enum Family { kDefault = -1, kSimple = 0, kPingPong = 1, kInterleaved = 2 };
+enum Family { kDefault = -1, kSimple = 0, kPingPong = 1 };
 
 struct Variant {
   const char *name;
-  int family;      // kernel family; 16-bit inputs only for kPingPong and kInterleaved
+  int family;      // kernel family; 16-bit inputs only for kPingPong
   int waves;       // waves per workgroup of the simple family (0 = per-shape default)
   int xcd_remap;
 };
@@ -36,8 +36,6 @@ const Variant kVariants[] = {
     {"simple_bm128_linear", kSimple, 4, 0},
     {"pingpong_bm256_xcd", kPingPong, 0, 1},
     {"pingpong_bm256_linear", kPingPong, 0, 0},
-    {"interleaved_bm128_xcd", kInterleaved, 0, 1},
-    {"interleaved_bm128_linear", kInterleaved, 0, 0},
     {"simple_bm256_xcd", kSimple, 8, 1},
     {"simple_bm256_linear", kSimple, 8, 0},
 };
@@ -62,7 +60,6 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
                                       : fa_simple_instance_bf16((int)D, causal != 0, waves);
       break;
     case kPingPong: *out = fa_pingpong_instance(dtype, (int)D, causal != 0); break;
-    case kInterleaved: *out = fa_interleaved_instance(dtype, (int)D, causal != 0); break;
     default: return false;
   }
   return out->fn != nullptr;
@@ -78,32 +75,35 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
 }
 
 int validate(const void *q, const void *k, const void *v, void *o, float *lse,
-             int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D,
-             float scale, int dtype) {
+             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t n_kv, int64_t D,
+             int causal_align, float scale, int dtype) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
-  if (n_kv < 0 || n_kv > N) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+  if (n_kv < 0 || n_kv > Nk) return FA_ERR_INVALID_ARG;
+  if (causal_align != FA_CAUSAL_TOP_LEFT && causal_align != FA_CAUSAL_BOTTOM_RIGHT) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   const int es = elem_bytes(dtype);
   if (es == 0) return FA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  // one head must be addressable with 32-bit byte offsets
-  if (N > (INT64_C(0x7fffffff) / (D * es))) return FA_ERR_UNSUPPORTED;
-  const int64_t tiles = (N + 127) / 128;
+  // one head of Q/O and of K/V must be addressable with 32-bit byte offsets
+  // (this also keeps every row index and the causal offset within int range)
+  if (Nq > (INT64_C(0x7fffffff) / (D * es)) || Nk > (INT64_C(0x7fffffff) / (D * es)))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t tiles = (Nq + 127) / 128;
   if (B > INT64_C(0x7fffffff) / H || B * H > INT64_C(0x7fffffff) / tiles) return FA_ERR_UNSUPPORTED;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
                         reinterpret_cast<uintptr_t>(lse);
   if (mis & 15) return FA_ERR_ALIGNMENT;
-  const int64_t tbytes = B * H * N * D * es;  // < 2^62 given the limits above
-  const void *ins[3] = {q, k, v};
-  for (const void *x : ins)
-    if (overlaps(o, tbytes, x, tbytes)) return FA_ERR_INVALID_ARG;
+  const int64_t qbytes = B * H * Nq * D * es;  // < 2^62 given the limits above
+  const int64_t kbytes = B * H * Nk * D * es;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) || overlaps(o, qbytes, v, kbytes))
+    return FA_ERR_INVALID_ARG;
   if (lse) {
-    const int64_t lbytes = B * H * N * (int64_t)sizeof(float);
-    for (const void *x : ins)
-      if (overlaps(lse, lbytes, x, tbytes)) return FA_ERR_INVALID_ARG;
-    if (overlaps(lse, lbytes, o, tbytes)) return FA_ERR_INVALID_ARG;
+    const int64_t lbytes = B * H * Nq * (int64_t)sizeof(float);
+    if (overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, k, kbytes) ||
+        overlaps(lse, lbytes, v, kbytes) || overlaps(lse, lbytes, o, qbytes))
+      return FA_ERR_INVALID_ARG;
   }
   return FA_OK;
 }
@@ -111,9 +111,9 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse,
 void opt_in_lds(const void *fn, int bytes);
 
 int launch(const void *q, const void *k, const void *v, void *o, float *lse,
-           int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D, int causal,
-           float scale, int dtype, void *stream, int variant) {
-  int rc = validate(q, k, v, o, lse, B, H, N, n_kv, D, scale, dtype);
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t n_kv, int64_t D, int causal,
+           int causal_align, float scale, int dtype, void *stream, int variant) {
+  int rc = validate(q, k, v, o, lse, B, H, Nq, Nk, n_kv, D, causal_align, scale, dtype);
   if (rc != FA_OK) return rc;
   if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
   FaLaunch L;
@@ -126,9 +126,12 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   p.v = v;
   p.o = o;
   p.lse = lse;
-  p.N = N;
+  p.nq = Nq;
+  p.nk = Nk;
   p.n_kv = n_kv;
-  p.nq_tiles = (int)((N + L.bm - 1) / L.bm);
+  // top-left: query i sees keys j <= i; bottom-right: j <= i + (Nk - Nq)
+  p.coff = causal_align == FA_CAUSAL_BOTTOM_RIGHT ? Nk - Nq : 0;
+  p.nq_tiles = (int)((Nq + L.bm - 1) / L.bm);
   p.xcd_remap = kVariants[variant].xcd_remap;
   // scale * log2(e), formed in double and rounded once
   p.c = (float)((double)scale * 1.4426950408889634);
@@ -161,10 +164,17 @@ void opt_in_lds(const void *fn, int bytes) {
 
 extern "C" {
 
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+              int causal_align, float scale, int dtype, void *stream) {
+  return launch(q, k, v, o, lse, B, H, Nq, Nk, Nk, D, causal, causal_align, scale, dtype, stream, 0);
+}
+
 int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse,
                    int64_t B, int64_t H, int64_t N, int64_t n_kv, int64_t D,
                    int causal, float scale, int dtype, void *stream, int variant) {
-  return launch(q, k, v, o, lse, B, H, N, n_kv, D, causal, scale, dtype, stream, variant);
+  return launch(q, k, v, o, lse, B, H, N, N, n_kv, D, causal, FA_CAUSAL_TOP_LEFT, scale, dtype,
+                stream, variant);
 }
 
 int fa_fwd_nk(const void *q, const void *k, const void *v, void *o, float *lse,

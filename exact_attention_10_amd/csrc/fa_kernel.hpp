@@ -27,9 +27,11 @@
 // ends with O = 0, LSE = -inf ("Triton: FlashAttention-2 Forward Pass", The
 // rescale direction).
 //
-// Causal attention (top-left) stops the key loop after the tile's last query
-// row and applies the element mask only on tiles that straddle the diagonal
-// or the end of the keys ("A09", section 3, Causal masking: skipping beats
+// Causal attention stops the key loop after the tile's last query row and
+// applies the element mask only on tiles that straddle the diagonal or the
+// end of the keys. The diagonal is shifted by coff: 0 aligns it top-left,
+// nk - nq bottom-right ("How to profile and optimise kernels", Round 4,
+// on non-square causal attention) ("A09", section 3, Causal masking: skipping beats
 // masking; "How to profile and optimise kernels", Round 4).
 #pragma once
 
@@ -63,9 +65,11 @@ struct Params {
   const void *q, *k, *v;
   void *o;
   float *lse;          // may be null
-  int64_t N;           // rows per head (query and key length)
-  int64_t n_kv;        // keys j >= n_kv are masked (n_kv <= N)
-  int nq_tiles;        // ceil(N / BM)
+  int64_t nq;          // query (and output) rows per head
+  int64_t nk;          // key and value rows per head
+  int64_t n_kv;        // keys j >= n_kv are masked (n_kv <= nk)
+  int64_t coff;        // causal: query i sees keys j <= i + coff
+  int nq_tiles;        // ceil(nq / BM)
   int xcd_remap;       // 1: map workgroups so that one XCD works on few heads
   float c;             // scale * log2(e)
 };
@@ -200,26 +204,31 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   const int bh = bid / p.nq_tiles;
   int qt = bid - bh * p.nq_tiles;
   if (CAUSAL) qt = p.nq_tiles - 1 - qt;    // longest causal tiles first
-  const int64_t N = p.N;
+  // Query and key lengths are separate ("Triton: FlashAttention-2 Forward
+  // Pass", Masks and sentinels): Q rows, the output and LSE use nq; the key
+  // loop and the K/V rows use nk (and the key-length mask n_kv).
+  const int64_t Nq = p.nq;
   const int q0 = qt * BM;
   const int qw = q0 + wave * 32;           // first query row of this wave
   const int my_q = qw + l32;               // the query row this lane owns
+  const int coff = (int)p.coff;            // causal diagonal: key j visible when j <= i + coff
 
-  const int64_t head_elems = N * (int64_t)D;
-  const char *qh = (const char *)p.q + (int64_t)bh * head_elems * ES;
-  const char *kh = (const char *)p.k + (int64_t)bh * head_elems * ES;
-  const char *vh = (const char *)p.v + (int64_t)bh * head_elems * ES;
+  const int64_t q_head = Nq * (int64_t)D;      // elements per head of Q and O
+  const int64_t k_head = p.nk * (int64_t)D;    // elements per head of K and V
+  const char *qh = (const char *)p.q + (int64_t)bh * q_head * ES;
+  const char *kh = (const char *)p.k + (int64_t)bh * k_head * ES;
+  const char *vh = (const char *)p.v + (int64_t)bh * k_head * ES;
 
   const int n_kv = (int)p.n_kv;
   int kend = n_kv;
-  if (CAUSAL) kend = min(kend, q0 + BM);
+  if (CAUSAL) kend = min(kend, q0 + BM + coff);
   const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
   // ---- Q fragments (B operand of S^T = K Q^T), straight from global ----
   // lane (q = l32, half) holds Q[my_q][kc*KSTEP + half*KSTEP/2 ...]
   constexpr int QE = KSTEP / 2;             // elements per lane per fragment
   typedef uint16_t qraw_t __attribute__((ext_vector_type(8)));
-  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(head_elems * ES));
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(q_head * ES));
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
   // fragments stored as raw 32-bit words
@@ -227,7 +236,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   uint32_t qf[NKC][QW];
   {
     const uint32_t row_off = (uint32_t)my_q * RB;
-    const bool row_ok = my_q < N;
+    const bool row_ok = my_q < Nq;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const uint32_t off = row_off + (uint32_t)((kc * KSTEP + half * QE) * ES);
@@ -316,7 +325,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     if (t + 1 < n_tiles) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
 
     const int kstart = t * BN;
-    if (CAUSAL && kstart > qw + 31) return;   // every key of this tile is in this wave's future
+    if (CAUSAL && kstart > qw + 31 + coff) return;   // every key of this tile is in this wave's future
 
     const char *kl = smem + buf * (2 * C::TILE_BYTES);
     const char *vl = kl + C::TILE_BYTES;
@@ -377,14 +386,14 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     }
 
     // ---- masks: only on tiles past the end of the keys or on the diagonal ----
-    const bool need_mask = (kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw);
+    const bool need_mask = (kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw + coff);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kstart + kb * 32 + 8 * (i / 4) + half * 4 + (i % 4);
-          const bool bad = (key >= n_kv) || (CAUSAL && key > my_q);
+          const bool bad = (key >= n_kv) || (CAUSAL && key > my_q + coff);
           if (bad) s[kb][i] = -INFINITY;
         }
     }
@@ -475,8 +484,8 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   // ---- finalize: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_q < N) {
-    char *orow = (char *)p.o + ((int64_t)bh * head_elems + (int64_t)my_q * D) * ES;
+  if (my_q < Nq) {
+    char *orow = (char *)p.o + ((int64_t)bh * q_head + (int64_t)my_q * D) * ES;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -494,7 +503,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
       }
     if (p.lse && half == 0) {
       const float lse = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
-      p.lse[(int64_t)bh * N + my_q] = lse;
+      p.lse[(int64_t)bh * Nq + my_q] = lse;
     }
   }
 }

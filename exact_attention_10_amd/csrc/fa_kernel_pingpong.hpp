@@ -85,26 +85,28 @@ __global__ void __launch_bounds__(512, 1) fa_fwd_pingpong_kernel(Params p) {
   const int bh = bid / p.nq_tiles;
   int qt = bid - bh * p.nq_tiles;
   if (CAUSAL) qt = p.nq_tiles - 1 - qt;
-  const int64_t N = p.N;
+  const int64_t Nq = p.nq;
   const int q0 = qt * BM;
   const int qw = q0 + wave * 32;
   const int my_q = qw + l32;
+  const int coff = (int)p.coff;            // causal: key j visible to query i when j <= i + coff
 
-  const int64_t head_elems = N * (int64_t)D;
-  const char *qh = (const char *)p.q + (int64_t)bh * head_elems * 2;
-  const char *kh = (const char *)p.k + (int64_t)bh * head_elems * 2;
-  const char *vh = (const char *)p.v + (int64_t)bh * head_elems * 2;
+  const int64_t q_head = Nq * (int64_t)D;      // elements per head of Q and O
+  const int64_t k_head = p.nk * (int64_t)D;    // elements per head of K and V
+  const char *qh = (const char *)p.q + (int64_t)bh * q_head * 2;
+  const char *kh = (const char *)p.k + (int64_t)bh * k_head * 2;
+  const char *vh = (const char *)p.v + (int64_t)bh * k_head * 2;
   const int n_kv = (int)p.n_kv;
   int kend = n_kv;
-  if (CAUSAL) kend = min(kend, q0 + BM);
+  if (CAUSAL) kend = min(kend, q0 + BM + coff);
   const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
   // ---- Q fragments of this wave's 32 rows ----
   uint32_t qf[NKC][4];
   {
-    const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(head_elems * 2));
+    const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(q_head * 2));
     const uint32_t row_off = (uint32_t)my_q * RB;
-    const bool row_ok = my_q < N;
+    const bool row_ok = my_q < Nq;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const uint32_t off = row_off + (uint32_t)((kc * 16 + half * 8) * 2);
@@ -173,7 +175,7 @@ __global__ void __launch_bounds__(512, 1) fa_fwd_pingpong_kernel(Params p) {
   const float c = p.c;
 
   // a tile is visible to this wave unless every key is in the wave's future
-  auto visible = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < n_tiles && (!CAUSAL || t * BN <= qw + 31); };
+  auto visible = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < n_tiles && (!CAUSAL || t * BN <= qw + 31 + coff); };
 
   auto mfma16 = [&](u32x4 a, u32x4 b, f32x16 cin) __attribute__((always_inline)) -> f32x16 {
     if constexpr (DT == DT_BF16)
@@ -227,13 +229,13 @@ __global__ void __launch_bounds__(512, 1) fa_fwd_pingpong_kernel(Params p) {
   auto softmax = [&](int t) __attribute__((always_inline)) {
     if (!visible(t)) return;
     const int kstart = t * BN;
-    if ((kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw)) {
+    if ((kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw + coff)) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kstart + kb * 32 + 8 * (i / 4) + half * 4 + (i % 4);
-          if ((key >= n_kv) || (CAUSAL && key > my_q)) s[kb][i] = -INFINITY;
+          if ((key >= n_kv) || (CAUSAL && key > my_q + coff)) s[kb][i] = -INFINITY;
         }
     }
     float mx = s[0][0];
@@ -313,8 +315,8 @@ __global__ void __launch_bounds__(512, 1) fa_fwd_pingpong_kernel(Params p) {
   // ---- finalize ----
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_q < N) {
-    char *orow = (char *)p.o + ((int64_t)bh * head_elems + (int64_t)my_q * D) * 2;
+  if (my_q < Nq) {
+    char *orow = (char *)p.o + ((int64_t)bh * q_head + (int64_t)my_q * D) * 2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -326,7 +328,7 @@ __global__ void __launch_bounds__(512, 1) fa_fwd_pingpong_kernel(Params p) {
       }
     if (p.lse && half == 0) {
       const float lse = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
-      p.lse[(int64_t)bh * N + my_q] = lse;
+      p.lse[(int64_t)bh * Nq + my_q] = lse;
     }
   }
 }

@@ -18,4 +18,3 @@ FaLaunch fa_simple_instance_fp32(int d, bool causal, int waves);
 FaLaunch fa_simple_instance_fp16(int d, bool causal, int waves);
 FaLaunch fa_simple_instance_bf16(int d, bool causal, int waves);
 FaLaunch fa_pingpong_instance(int dt, int d, bool causal);
-FaLaunch fa_interleaved_instance(int dt, int d, bool causal);

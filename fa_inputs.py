@@ -108,6 +108,18 @@ def draw_qkv(B, H, N, D, dtype, seed, q_mult=1.0, v_dist="normal"):
     return tuple(round_to_dtype(t, dtype) for t in (q, k, v))
 
 
+def draw_qkv_cross(B, H, Nq, Nk, D, dtype, seed):
+    """Q of shape [B, H, Nq, D] and K, V of shape [B, H, Nk, D] (query and key
+    lengths differ), drawn N(0,1) in the same order and rounding as draw_qkv."""
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Nq, D), dtype=np.float32)
+    k = rng.standard_normal((B, H, Nk, D), dtype=np.float32)
+    v = rng.standard_normal((B, H, Nk, D), dtype=np.float32)
+    return tuple(round_to_dtype(t, dtype) for t in (q, k, v))
+
+
 def workload_inputs(w: Workload, N: int | None = None, B: int | None = None,
                     H: int | None = None):
     """Inputs of a workload (optionally at a different B/H/N, same recipe)."""

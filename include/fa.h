@@ -17,10 +17,13 @@
  * Conventions shared by every entry point:
  *  - q, k, v, o are device pointers to contiguous row-major [B, H, N, D]
  *    tensors of element type `dtype`; o has the same type as the inputs.
- *  - lse is a device pointer to a contiguous fp32 [B, H, N] tensor, or NULL
- *    (then the log-sum-exp is not written). LSE uses the natural log.
+ *    (fa_fwd_ex: q and o are [B, H, Nq, D], k and v are [B, H, Nk, D].)
+ *  - lse is a device pointer to a contiguous fp32 [B, H, N] tensor ([B, H, Nq]
+ *    for fa_fwd_ex), or NULL (then the log-sum-exp is not written). LSE uses
+ *    the natural log.
  *  - causal != 0 applies the top-left causal mask: query i sees key j only
  *    when j <= i ("Building a Verifiable FlashAttention Forward", Part 1).
+ *    fa_fwd_ex can align the mask bottom-right instead.
  *  - scale multiplies Q K^T; it must be finite and > 0 (the usual value is
  *    1/sqrt(D)).
  *  - Ownership: the caller owns every buffer; the library allocates no device
@@ -33,9 +36,9 @@
  *  - Error behaviour: every argument is validated before any HIP call. On an
  *    invalid argument nothing is launched and a negative code is returned;
  *    the outputs are left untouched. Thread-safe and reentrant.
- *  - Limits: 1 <= B, H, N; B*H*ceil(N/128) < 2^31 workgroups; one head's
- *    tensor (N*D*element size bytes) must be below 2^31 bytes; pointers must
- *    be 16-byte aligned.
+ *  - Limits: 1 <= B, H, N (Nq, Nk); B*H*ceil(N/128) < 2^31 workgroups; one
+ *    head's tensor (N*D*element size bytes) must be below 2^31 bytes;
+ *    pointers must be 16-byte aligned.
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
@@ -47,6 +50,12 @@ extern "C" {
 #endif
 
 enum fa_dtype { FA_DTYPE_FP32 = 0, FA_DTYPE_FP16 = 1, FA_DTYPE_BF16 = 2 };
+
+/* Alignment of the causal mask when the query and key lengths differ. */
+enum fa_causal_align {
+  FA_CAUSAL_TOP_LEFT = 0,     /* query i sees keys j <= i                   */
+  FA_CAUSAL_BOTTOM_RIGHT = 1  /* query i sees keys j <= i + (Nk - Nq)       */
+};
 
 enum fa_status {
   FA_OK = 0,
@@ -64,6 +73,27 @@ enum fa_status {
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
            int dtype, void *stream);
+
+/*
+ * Attention forward with separate query and key/value lengths (cross
+ * attention): q, o [B,H,Nq,D]; k, v [B,H,Nk,D]; lse [B,H,Nq] or NULL. The
+ * grid, the query-row mask, the store and LSE use Nq; the key loop, the K/V
+ * loads and the score mask use Nk ("Triton: FlashAttention-2 Forward Pass",
+ * Masks and sentinels, on cross-attention). With causal != 0, causal_align
+ * selects the diagonal: FA_CAUSAL_TOP_LEFT (query i sees keys j <= i, the
+ * convention "How to profile and optimise kernels", Round 4, attributes to
+ * SDPA's is_causal) or FA_CAUSAL_BOTTOM_RIGHT (j <= i + Nk - Nq, which the
+ * same passage attributes to the FlashAttention library since 2.1); it is
+ * ignored when causal == 0 and must still be one of the two values. A query
+ * row that sees no key (bottom-right with Nq > Nk: rows i < Nq - Nk) gets
+ * O = 0 and LSE = -inf. Requires 1 <= Nq, 1 <= Nk; the other limits and the
+ * error codes are those of fa_fwd (FA_ERR_INVALID_ARG also for an unknown
+ * causal_align). fa_fwd(..., N, ...) equals fa_fwd_ex(..., N, N, ...).
+ */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+              int causal, int causal_align, float scale, int dtype,
+              void *stream);
 
 /*
  * As fa_fwd, with only the first n_kv keys (0 <= n_kv <= N) visible: keys

@@ -91,6 +91,12 @@ def reference_full(q_bits, k_bits, v_bits, dtype, scale, causal, n_kv=None):
     return oracle.attention(q, k, v, scale, causal, n_kv=n_kv)
 
 
+def reference_full_ex(q_bits, k_bits, v_bits, dtype, scale, causal, causal_align):
+    """Oracle for separate query and key lengths (q [B,H,Nq,D], k/v [B,H,Nk,D])."""
+    q, k, v = (fa_inputs.to_f32(x, dtype) for x in (q_bits, k_bits, v_bits))
+    return oracle.attention(q, k, v, scale, causal, causal_align=causal_align)
+
+
 def reference_rows(q_bits, k_bits, v_bits, dtype, scale, causal, rows, n_kv=None):
     q, k, v = (fa_inputs.to_f32(x, dtype) for x in (q_bits, k_bits, v_bits))
     return oracle.attention_rows(q, k, v, scale, causal, rows, n_kv=n_kv)

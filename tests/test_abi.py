@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
+    for n in ("fa_fwd", "fa_fwd_ex", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
               "fa_num_variants", "fa_variant_name"):
         assert n in names
 
@@ -95,6 +95,32 @@ def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, N=256, D=128, causal=0, scale
 ])
 def test_validation_rejects_before_any_hip_call(lib, kw, code):
     assert call(lib, **kw) == code
+
+
+def call_ex(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=256, Nk=512, D=128, causal=1,
+            align=fa.FA_CAUSAL_BOTTOM_RIGHT, scale=0.088, dtype=fa.FA_DTYPE_BF16):
+    return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, D, causal, align, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(align=2), fa.FA_ERR_INVALID_ARG),
+    (dict(align=-1, causal=0), fa.FA_ERR_INVALID_ARG),     # checked even without a mask
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=1 << 24, dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),   # K head > 2 GiB
+    (dict(Nq=1 << 24, dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),   # Q head > 2 GiB
+    (dict(v=V + 8), fa.FA_ERR_ALIGNMENT),
+    # o is [2,4,256,128] bf16 = 512 KiB; k and v are [2,4,512,128] = 1 MiB each
+    (dict(o=K + (1 << 20) - 4096), fa.FA_ERR_INVALID_ARG),  # o overlaps the end of k
+    (dict(k=O + (1 << 19) - 256), fa.FA_ERR_INVALID_ARG),   # k starts inside o
+    (dict(lse=V + (1 << 20) - 64), fa.FA_ERR_INVALID_ARG),  # lse inside v's key-length extent
+])
+def test_cross_attention_validation(lib, kw, code):
+    assert call_ex(lib, **kw) == code
 
 
 def test_lse_may_be_null_for_validation(lib):

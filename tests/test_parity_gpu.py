@@ -12,6 +12,7 @@ import pytest
 
 import exact_attention_10_amd as fa
 import fa_inputs
+import oracle
 from tests import parity
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +99,86 @@ def test_variants(variant, causal, dtype, D):
         if linear:
             o2, l2 = _run(qb, kb, vb, dtype, causal, scale, variant=linear[0])
             assert np.array_equal(o, o2) and np.array_equal(lse, l2), "workgroup order changed bits"
+
+
+# ---------------------------------------------------------------------------
+# Separate query and key lengths (fa_fwd_ex), both causal alignments
+
+
+def _run_ex(qb, kb, vb, dtype, causal, align, scale):
+    import torch
+    q, k, v = (parity.to_device(x, dtype) for x in (qb, kb, vb))
+    o, lse = fa.fa_fwd_ex(q, k, v, causal=causal, causal_align=align, scale=scale)
+    torch.cuda.synchronize()
+    return parity.from_device(o), lse.cpu().numpy()
+
+
+CROSS_SHAPES = [(1, 2), (37, 200), (200, 37), (128, 300), (300, 129), (1, 513), (64, 64)]
+MASKS = [(False, "top-left"), (True, "top-left"), (True, "bottom-right")]
+
+
+@pytest.mark.parametrize("causal,align", MASKS)
+@pytest.mark.parametrize("nq,nk", CROSS_SHAPES)
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64), ("bf16", 64), ("fp32", 64)])
+def test_cross_attention_full_parity(dtype, D, nq, nk, causal, align):
+    _banner(f"cross dtype={dtype} D={D} Nq={nq} Nk={nk} causal={causal} {align}")
+    B, H = 2, 3
+    seed = 3000 + nq * 7 + nk + D + DTYPES.index(dtype) + (11 if causal else 0) + (5 if align == "bottom-right" else 0)
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, dtype, seed)
+    scale = parity.default_scale(D)
+    o, lse = _run_ex(qb, kb, vb, dtype, causal, align, scale)
+    o_ref, lse_ref = parity.reference_full_ex(qb, kb, vb, dtype, scale, causal, align)
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"cross {dtype} D={D} {nq}x{nk} {causal} {align}")
+
+
+def test_cross_attention_one_query_two_keys():
+    """One query, two keys, equal scores, value rows 5 and 10: O = 7.5 and
+    LSE = ln 2 exactly representable; top-left causal sees key 0 only (O = 5)."""
+    import torch
+    _banner("cross one query two keys")
+    D = 64
+    q = torch.zeros(1, 1, 1, D, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(1, 1, 2, D, device="cuda").to(torch.bfloat16)
+    v = torch.tensor([5.0, 10.0], device="cuda").view(1, 1, 2, 1).expand(1, 1, 2, D)
+    v = v.to(torch.bfloat16).contiguous()
+    for causal, align, want, lse_want in ((False, "top-left", 7.5, math.log(2.0)),
+                                          (True, "bottom-right", 7.5, math.log(2.0)),
+                                          (True, "top-left", 5.0, 0.0)):
+        o, lse = fa.fa_fwd_ex(q, k, v, causal=causal, causal_align=align)
+        torch.cuda.synchronize()
+        assert (o.float() == want).all(), (causal, align, o.float().unique())
+        assert abs(float(lse) - lse_want) <= 1e-6, (causal, align, float(lse))
+
+
+def test_cross_attention_equal_lengths_match_fa_fwd():
+    """fa_fwd_ex with Nq = Nk (either alignment) is bit-identical to fa_fwd."""
+    import torch
+    _banner("cross equal lengths == fa_fwd")
+    qb, kb, vb = fa_inputs.draw_qkv(2, 4, 333, 128, "bf16", 77)
+    q, k, v = (parity.to_device(x, "bf16") for x in (qb, kb, vb))
+    for causal in (False, True):
+        o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
+        for align in ("top-left", "bottom-right"):
+            o2, l2 = fa.fa_fwd_ex(q, k, v, causal=causal, causal_align=align)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_cross_attention_long_keys_sampled():
+    """A longer cross-attention case (Nq = 1000, Nk = 5000, D = 128, bf16,
+    causal bottom-right) checked on sampled rows, including the first rows,
+    whose visible range starts at Nk - Nq keys."""
+    _banner("cross long keys sampled rows")
+    B, H, nq, nk, D = 1, 4, 1000, 5000, 128
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, "bf16", 4242)
+    scale = parity.default_scale(D)
+    o, lse = _run_ex(qb, kb, vb, "bf16", True, "bottom-right", scale)
+    rows = parity.sample_rows(B, H, nq, 200, 99)
+    q, k, v = (fa_inputs.to_f32(x, "bf16") for x in (qb, kb, vb))
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, True, rows, causal_align="bottom-right")
+    o_s = o.reshape(B * H, nq, D)[rows[:, 0], rows[:, 1]]
+    l_s = lse.reshape(B * H, nq)[rows[:, 0], rows[:, 1]]
+    parity.check(o_s, l_s, o_ref, lse_ref, "bf16", "cross long keys")
 
 
 def test_no_lse_output():
