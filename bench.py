@@ -93,17 +93,25 @@ def _device_inputs(w, torch):
     return (dev(qb), dev(kb), dev(vb)), (qb, kb, vb)
 
 
-def time_gpu(w, causal, steps, warmup, torch, fa, variant=None):
+def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False):
     """Whole-run timing: `warmup` untimed calls, then `steps` calls bracketed
-    by synchronisation and events on the launch stream (fa_fwd, or kernel
-    variant `variant` through fa_fwd_variant)."""
+    by synchronisation and events on the launch stream (fa_fwd, kernel
+    variant `variant` through fa_fwd_variant, or fa_fwd_splitkv with the
+    library's split choice and a workspace allocated before timing)."""
     (q, k, v), _ = _device_inputs(w, torch)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
+    ws = None
+    if splitkv:
+        need = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.N, w.N, w.D, 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
 
     def call():
-        if variant is None:
+        if splitkv:
+            fa.fa_fwd_splitkv(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream,
+                              num_splits=0, workspace=ws)
+        elif variant is None:
             fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
         else:
             fa.fa_fwd_variant(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream,
@@ -221,6 +229,25 @@ def main():
                           "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
             print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
                   flush=True)
+        # small grids: the [B=8, N=1024, D=64] workload (64 workgroups of 128
+        # query rows) and a [B=1, H=8, N=2048, D=128] one (128 workgroups),
+        # single pass against split-KV with the library's split choice
+        smalls = (fa_inputs.WORKLOADS["b8h1_n1024_d64_bf16"],
+                  fa_inputs.Workload("b1h8_n2048_d128_bf16", 1, 8, 2048, 128, "bf16", 7, (False,)))
+        for small in smalls:
+            for causal in small.masks:
+                for split in (False, True):
+                    r = time_gpu(small, causal, max(20, a.steps), max(10, a.warmup), torch, fa,
+                                 splitkv=split)
+                    key = (f"{small.name}_{'causal' if causal else 'noncausal'}"
+                           f"_{'splitkv' if split else 'single_pass'}")
+                    extra[key] = {"ms": round(r["ms"], 5), "tflops": round(r["tflops"], 2),
+                                  "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
+                    if split:
+                        extra[key]["num_splits"] = fa.fa_splitkv_auto_splits(
+                            small.B, small.H, small.N, small.N, small.D)
+                    print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s",
+                          file=sys.stderr, flush=True)
 
     esize = fa_inputs.ESIZE[w.dtype]
     roofline = {

@@ -10,6 +10,8 @@ The functions mirror the C ABI of ``include/fa.h``:
 * :func:`fa_fwd` -- O = softmax(scale * Q K^T) V and the row log-sum-exp;
 * :func:`fa_fwd_ex` -- the same with separate query and key lengths and a
   top-left or bottom-right causal mask;
+* :func:`fa_fwd_splitkv` -- the same result for small grids, with the keys
+  of every query tile split over several workgroups and combined;
 * :func:`fa_fwd_nk` -- the same with only the first ``n_kv`` keys visible;
 * :func:`fa_fwd_variant` -- run a named kernel variant (tuning);
 * :func:`fa_num_variants`, :func:`fa_variant_name`, :func:`fa_strerror`,
@@ -34,6 +36,10 @@ _P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
+    "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _I,
+                            _P, ctypes.c_size_t, _P]),
+    "fa_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I]),
+    "fa_splitkv_auto_splits": (_I, [_I64, _I64, _I64, _I64, _I64]),
     "fa_fwd_nk": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_fwd_variant": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P, _I]),
     "fa_num_variants": (_I, []),
@@ -192,6 +198,45 @@ def fa_fwd_ex(q, k, v, o=None, lse=None, *, causal=False, causal_align="top-left
                        _dtype_code(q), _stream_handle(q, stream))
     _check(rc)
     return o, lse
+
+
+def fa_fwd_splitkv(q, k, v, o=None, lse=None, *, causal=False, causal_align="top-left",
+                   scale=None, num_splits=0, workspace=None, stream=None, with_lse=True):
+    """Split-KV attention (same result as :func:`fa_fwd_ex`); returns (o, lse).
+
+    ``num_splits`` = 0 lets the library choose. ``workspace`` is a device tensor
+    of at least :func:`fa_fwd_splitkv_workspace_size` bytes; when None, one is
+    allocated here with torch (the library itself allocates nothing).
+    """
+    import torch
+    lib = load_library()
+    if causal_align not in _ALIGN:
+        raise ValueError(f"causal_align must be one of {sorted(_ALIGN)}")
+    o, lse = _prepare(q, k, v, o, lse, with_lse, same_length=False)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = lib.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, int(num_splits))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr() if lse is not None else None,
+                            B, H, Nq, Nk, D, int(bool(causal)), _ALIGN[causal_align],
+                            float(scale), _dtype_code(q), int(num_splits), ws_ptr, ws_bytes,
+                            _stream_handle(q, stream))
+    _check(rc)
+    return o, lse
+
+
+def fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits=0) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, int(num_splits)))
+
+
+def fa_splitkv_auto_splits(B, H, Nq, Nk, D) -> int:
+    return int(load_library().fa_splitkv_auto_splits(B, H, Nq, Nk, D))
 
 
 def fa_num_variants() -> int:

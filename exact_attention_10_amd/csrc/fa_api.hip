@@ -6,9 +6,11 @@
 // library allocates no memory and keeps no state; a launch is asynchronous on
 // the caller's stream.
 #include "fa.h"
+#include "fa_combine.hpp"
 #include "fa_kernel.hpp"
 #include "fa_launch.hpp"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -148,6 +150,105 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   return FA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Split-KV: each (head, query tile) is split into n_splits shares of its key
+// tiles, so a small grid still fills the chip; a second kernel combines the
+// fp32 partials through their log-sum-exps.
+
+constexpr int kSplitBM = 128;          // query rows per workgroup of the split kernel
+
+int64_t split_grid(int64_t B, int64_t H, int64_t Nq) { return B * H * ((Nq + kSplitBM - 1) / kSplitBM); }
+
+// Measured on MI355X: splitting pays only when the single-pass grid leaves
+// most CUs idle and each split keeps enough key tiles to amortise the combine
+// pass (8 tiles of 64 keys at D = 128, 16 at D = 64, whose tiles cost less).
+// The splits then aim at about one workgroup per CU.
+int auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D) {
+  const int64_t g = split_grid(B, H, Nq);
+  if (g <= 0 || g > 128) return 1;
+  const int64_t tiles = (Nk + 63) / 64;
+  int64_t ns = std::min<int64_t>((256 + g - 1) / g, tiles / (D == 64 ? 16 : 8));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(ns, fa::kMaxSplits));
+}
+
+// o_part at offset 0, lse_part at the next 256-byte boundary
+struct SplitLayout {
+  int64_t lse_off;
+  int64_t bytes;
+};
+SplitLayout split_layout(int64_t B, int64_t H, int64_t Nq, int64_t D, int ns) {
+  const int64_t rows = B * H * Nq;
+  const int64_t o_bytes = (int64_t)ns * rows * D * (int64_t)sizeof(float);
+  const int64_t lse_off = (o_bytes + 255) / 256 * 256;
+  return {lse_off, lse_off + (int64_t)ns * rows * (int64_t)sizeof(float)};
+}
+
+int launch_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                   int causal_align, float scale, int dtype, int num_splits, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, Nq, Nk, Nk, D, causal_align, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (num_splits < 0 || num_splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
+  const int ns = num_splits ? num_splits : auto_splits(B, H, Nq, Nk, D);
+  if (ns == 1)   // nothing to split: the single-pass kernel, workspace untouched
+    return launch(q, k, v, o, lse, B, H, Nq, Nk, Nk, D, causal, causal_align, scale, dtype, stream, 0);
+  const SplitLayout lay = split_layout(B, H, Nq, D, ns);
+  if (!workspace || (int64_t)workspace_bytes < lay.bytes) return FA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return FA_ERR_ALIGNMENT;
+  const int es = elem_bytes(dtype);
+  const int64_t qbytes = B * H * Nq * D * es, kbytes = B * H * Nk * D * es;
+  if (overlaps(workspace, lay.bytes, q, qbytes) || overlaps(workspace, lay.bytes, k, kbytes) ||
+      overlaps(workspace, lay.bytes, v, kbytes) || overlaps(workspace, lay.bytes, o, qbytes) ||
+      (lse && overlaps(workspace, lay.bytes, lse, B * H * Nq * (int64_t)sizeof(float))))
+    return FA_ERR_INVALID_ARG;
+  if (split_grid(B, H, Nq) > INT64_C(0x7fffffff) / ns) return FA_ERR_UNSUPPORTED;
+
+  const FaLaunch L = fa_splitkv_instance(dtype, (int)D, causal != 0);
+  const void *comb = fa_combine_instance(dtype, (int)D);
+  if (!L.fn || !comb) return FA_ERR_UNSUPPORTED;
+  if (L.lds > 65536) opt_in_lds(L.fn, L.lds);
+
+  fa::Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.nq = Nq;
+  p.nk = Nk;
+  p.n_kv = Nk;
+  p.coff = causal_align == FA_CAUSAL_BOTTOM_RIGHT ? Nk - Nq : 0;
+  p.nq_tiles = (int)((Nq + L.bm - 1) / L.bm);
+  p.xcd_remap = 1;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.n_splits = ns;
+  p.n_heads = (int)(B * H);
+  p.o_part = static_cast<float *>(workspace);
+  p.lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.lse_off);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void *args[] = {&p};
+  hipError_t e = hipLaunchKernel(L.fn, dim3((unsigned)(B * H * ns * p.nq_tiles)), dim3((unsigned)L.threads),
+                                 args, (size_t)L.lds, st);
+  if (e == hipSuccess) {
+    fa::CombineParams cp;
+    cp.o_part = p.o_part;
+    cp.lse_part = p.lse_part;
+    cp.o = o;
+    cp.lse = lse;
+    cp.rows = B * H * Nq;
+    cp.n_splits = ns;
+    void *cargs[] = {&cp};
+    e = hipLaunchKernel(comb, dim3((unsigned)((cp.rows + 3) / 4)), dim3(256), cargs, 0, st);
+  }
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_error, sizeof(g_hip_error), "%s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 // Kernels that use more than 64 KB of LDS raise their limit once per process.
 void opt_in_lds(const void *fn, int bytes) {
   static std::mutex mu;
@@ -187,6 +288,27 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
            int dtype, void *stream) {
   return fa_fwd_variant(q, k, v, o, lse, B, H, N, N, D, causal, scale, dtype, stream, 0);
+}
+
+int fa_splitkv_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return 1;
+  return auto_splits(B, H, Nq, Nk, D);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                     int num_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1 || num_splits < 0 || num_splits > fa::kMaxSplits)
+    return 0;
+  const int ns = num_splits ? num_splits : auto_splits(B, H, Nq, Nk, D);
+  return ns == 1 ? 0 : (size_t)split_layout(B, H, Nq, D, ns).bytes;
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                   int causal_align, float scale, int dtype, int num_splits, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  return launch_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, causal, causal_align, scale, dtype,
+                        num_splits, workspace, workspace_bytes, stream);
 }
 
 int fa_num_variants(void) { return kNumVariants; }

@@ -72,7 +72,16 @@ struct Params {
   int nq_tiles;        // ceil(nq / BM)
   int xcd_remap;       // 1: map workgroups so that one XCD works on few heads
   float c;             // scale * log2(e)
+  // split-KV partials (split kernels only): each workgroup covers a share of
+  // its query tile's key tiles and writes a normalised fp32 O partial and its
+  // LSE; a second kernel combines the splits
+  int n_splits;        // 1 .. kMaxSplits
+  int n_heads;         // B*H
+  float *o_part;       // [n_splits][BH][nq][D]
+  float *lse_part;     // [n_splits][BH][nq]
 };
+
+constexpr int kMaxSplits = 32;
 
 // ---------------------------------------------------------------------------
 // Element traits. 16-bit types use the 32x32x16 MFMA (8 elements per lane per
@@ -173,7 +182,7 @@ struct Cfg {
 // per SIMD for fp32, whose Q fragments are twice as wide. With 8 waves the
 // workgroup holds both waves of every SIMD and shares each K/V tile between
 // 256 query rows, halving the global->LDS traffic per query row.
-template <int DT, int D, bool CAUSAL, int WAVES = 4>
+template <int DT, int D, bool CAUSAL, int WAVES = 4, bool SPLIT = false>
 __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_kernel(Params p) {
   static_assert(WAVES == 4 || (WAVES == 8 && DT != DT_FP32), "4 waves, or 8 for 16-bit inputs");
   using C = Cfg<DT, D, CAUSAL, WAVES>;
@@ -201,8 +210,14 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     // that XCD's L2.
     bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   }
-  const int bh = bid / p.nq_tiles;
-  int qt = bid - bh * p.nq_tiles;
+  int rest = bid / p.nq_tiles;
+  int qt = bid - rest * p.nq_tiles;
+  int split = 0;
+  if (SPLIT) {
+    split = rest % p.n_splits;
+    rest /= p.n_splits;
+  }
+  const int bh = rest;
   if (CAUSAL) qt = p.nq_tiles - 1 - qt;    // longest causal tiles first
   // Query and key lengths are separate ("Triton: FlashAttention-2 Forward
   // Pass", Masks and sentinels): Q rows, the output and LSE use nq; the key
@@ -223,6 +238,13 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   int kend = n_kv;
   if (CAUSAL) kend = min(kend, q0 + BM + coff);
   const int n_tiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // key tiles [t_begin, t_end) of this workgroup: all of them, or this
+  // split's even share of them (a split may be empty)
+  int t_begin = 0, t_end = n_tiles;
+  if (SPLIT) {
+    t_begin = (int)(((int64_t)split * n_tiles) / p.n_splits);
+    t_end = (int)(((int64_t)(split + 1) * n_tiles) / p.n_splits);
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T), straight from global ----
   // lane (q = l32, half) holds Q[my_q][kc*KSTEP + half*KSTEP/2 ...]
@@ -322,7 +344,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     constexpr int buf = decltype(buf_c)::value;
     wait_vmem();
     __syncthreads();                        // tile t visible; the other buffer is free
-    if (t + 1 < n_tiles) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
+    if (t + 1 < t_end) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
 
     const int kstart = t * BN;
     if (CAUSAL && kstart > qw + 31 + coff) return;   // every key of this tile is in this wave's future
@@ -475,15 +497,33 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     }
   };
 
-  if (n_tiles > 0) issue_tile(0, std::integral_constant<int, 0>{});
-  for (int t = 0; t < n_tiles; t += 2) {
+  if (t_begin < t_end) issue_tile(t_begin, std::integral_constant<int, 0>{});
+  for (int t = t_begin; t < t_end; t += 2) {
     step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < t_end) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- finalize: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (SPLIT) {
+    // this split's normalised partial in fp32 and its LSE (-inf if it saw no key)
+    if (my_q < Nq) {
+      const int64_t prow = ((int64_t)split * p.n_heads + bh) * Nq + my_q;
+      float *orow = p.o_part + prow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + 8 * gq + half * 4;
+          *(float4 *)(orow + d0) = float4{acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv,
+                                          acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
+        }
+      if (half == 0)
+        p.lse_part[prow] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+    return;
+  }
   if (my_q < Nq) {
     char *orow = (char *)p.o + ((int64_t)bh * q_head + (int64_t)my_q * D) * ES;
 #pragma unroll

@@ -43,6 +43,7 @@
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -94,6 +95,46 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
               int causal, int causal_align, float scale, int dtype,
               void *stream);
+
+/*
+ * Split-KV forward: the same result as fa_fwd_ex, for grids too small to fill
+ * the chip (few heads times query tiles, e.g. short query blocks). Each
+ * (batch*head, 128-row query tile) is split into num_splits shares of its key
+ * tiles; every share writes a normalised fp32 partial O_s and its row
+ * log-sum-exp LSE_s into `workspace`, and a second kernel on the same stream
+ * combines them as LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s
+ * (the rebasing of "A09 - Advanced Triton & FlashAttention", section 3, across
+ * key partitions; the pages name split-KV as the use of a consistent exponent
+ * base in "Building a Verifiable FlashAttention Forward from PyTorch to
+ * Triton", Part 3). Arguments as fa_fwd_ex, plus:
+ *  - num_splits: 1 .. 32, or 0 to let the library choose
+ *    (fa_splitkv_auto_splits). With one split the single-pass kernel runs
+ *    and the workspace is not used (it may then be NULL).
+ *  - workspace: device memory owned by the caller, 256-byte aligned, at least
+ *    fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits) bytes, not
+ *    overlapping any other argument. Its contents on entry do not matter;
+ *    the library allocates nothing. Calls that share a workspace must be
+ *    ordered (same stream, or synchronised).
+ * Errors: those of fa_fwd_ex; FA_ERR_INVALID_ARG for num_splits outside
+ * 0 .. 32, a NULL or too small workspace, or a workspace overlapping another
+ * argument; FA_ERR_ALIGNMENT for a workspace not 256-byte aligned.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
+                   float *lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                   int64_t D, int causal, int causal_align, float scale,
+                   int dtype, int num_splits, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_fwd_splitkv needs for these sizes and num_splits (0 =
+ * the library's choice); 0 when that is a single split, or for invalid sizes. */
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq,
+                                     int64_t Nk, int64_t D, int num_splits);
+
+/* The number of splits fa_fwd_splitkv picks for num_splits = 0: 1 when the
+ * single-pass grid (B*H*ceil(Nq/128) workgroups) exceeds 128; otherwise about
+ * one workgroup per CU (256 / grid), limited so that each split keeps at
+ * least 8 key tiles of 64 keys at D = 128 (16 at D = 64), and at most 32. */
+int fa_splitkv_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D);
 
 /*
  * As fa_fwd, with only the first n_kv keys (0 <= n_kv <= N) visible: keys

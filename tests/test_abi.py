@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_ex", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
+    for n in ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+              "fa_splitkv_auto_splits", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
               "fa_num_variants", "fa_variant_name"):
         assert n in names
 
@@ -121,6 +122,58 @@ def call_ex(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=256, Nk=512, D=128, cau
 ])
 def test_cross_attention_validation(lib, kw, code):
     assert call_ex(lib, **kw) == code
+
+
+WS = 0x60000000   # fake workspace address (256-byte aligned)
+
+
+def call_split(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=200, Nk=1000, D=64, causal=0,
+               align=fa.FA_CAUSAL_TOP_LEFT, scale=0.125, dtype=fa.FA_DTYPE_BF16, ns=4,
+               ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, ns)
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, causal, align, scale, dtype, ns,
+                              ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_size(lib):
+    # o_part: ns * rows * D fp32, rounded up to 256 bytes; then lse_part: ns * rows fp32
+    rows, D, ns = 1 * 2 * 200, 64, 4
+    o_bytes = ns * rows * D * 4
+    want = (o_bytes + 255) // 256 * 256 + ns * rows * 4
+    assert lib.fa_fwd_splitkv_workspace_size(1, 2, 200, 1000, D, ns) == want
+    assert lib.fa_fwd_splitkv_workspace_size(1, 2, 200, 1000, D, 1) == 0      # single pass
+    assert lib.fa_fwd_splitkv_workspace_size(1, 2, 200, 1000, D, 33) == 0     # invalid
+    assert lib.fa_fwd_splitkv_workspace_size(0, 2, 200, 1000, D, 4) == 0      # invalid
+
+
+def test_splitkv_auto_choice(lib):
+    # [1, 8, 2048] queries at D = 128: 128 workgroups, 32 key tiles -> 2 splits
+    assert lib.fa_splitkv_auto_splits(1, 8, 2048, 2048, 128) == 2
+    # [8, 1, 1024] at D = 64: 16 key tiles are too few to split
+    assert lib.fa_splitkv_auto_splits(8, 1, 1024, 1024, 64) == 1
+    # a large grid needs no split
+    assert lib.fa_splitkv_auto_splits(4, 16, 4096, 4096, 128) == 1
+    # one query tile, many keys: one workgroup per CU would be 256, capped at 32
+    assert lib.fa_splitkv_auto_splits(1, 1, 1, 1 << 20, 128) == 32
+    # one query tile, 64 key tiles at D = 128: 8 splits of 8 tiles
+    assert lib.fa_splitkv_auto_splits(1, 1, 100, 4096, 128) == 8
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ns=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(ns=33), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), fa.FA_ERR_INVALID_ARG),                # too small
+    (dict(ws=WS + 16), fa.FA_ERR_ALIGNMENT),                      # not 256-byte aligned
+    (dict(ws=Q), fa.FA_ERR_INVALID_ARG),                          # overlaps q
+    (dict(ws=O - 256), fa.FA_ERR_INVALID_ARG),                    # runs into o
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),                          # checked like fa_fwd_ex
+    (dict(align=5), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+])
+def test_splitkv_validation(lib, kw, code):
+    assert call_split(lib, **kw) == code
 
 
 def test_lse_may_be_null_for_validation(lib):

@@ -181,6 +181,105 @@ def test_cross_attention_long_keys_sampled():
     parity.check(o_s, l_s, o_ref, lse_ref, "bf16", "cross long keys")
 
 
+# ---------------------------------------------------------------------------
+# Split-KV (fa_fwd_splitkv): the same attention, keys split over workgroups
+
+
+def _run_split(qb, kb, vb, dtype, causal, align, scale, num_splits, poison=True):
+    import torch
+    q, k, v = (parity.to_device(x, dtype) for x in (qb, kb, vb))
+    B, H, nq, D = q.shape
+    nk = k.shape[2]
+    need = fa.fa_fwd_splitkv_workspace_size(B, H, nq, nk, D, num_splits)
+    ws = None
+    if need:
+        # the workspace's contents on entry must not matter: fill it with NaNs
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        if poison:
+            ws.view(torch.float32)[: need // 4].fill_(float("nan"))
+    o, lse = fa.fa_fwd_splitkv(q, k, v, causal=causal, causal_align=align, scale=scale,
+                               num_splits=num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return parity.from_device(o), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("num_splits", [2, 5, 32])
+@pytest.mark.parametrize("causal,align", MASKS)
+@pytest.mark.parametrize("nq,nk", [(37, 200), (128, 300), (300, 129), (1, 513), (200, 37)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64), ("fp32", 64)])
+def test_splitkv_full_parity(dtype, D, nq, nk, causal, align, num_splits):
+    _banner(f"splitkv dtype={dtype} D={D} Nq={nq} Nk={nk} causal={causal} {align} splits={num_splits}")
+    B, H = 2, 2
+    seed = 5000 + nq + 3 * nk + D + num_splits + DTYPES.index(dtype) + (7 if causal else 0)
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, dtype, seed)
+    scale = parity.default_scale(D)
+    o, lse = _run_split(qb, kb, vb, dtype, causal, align, scale, num_splits)
+    o_ref, lse_ref = parity.reference_full_ex(qb, kb, vb, dtype, scale, causal, align)
+    parity.check(o, lse, o_ref, lse_ref, dtype,
+                 f"splitkv {dtype} D={D} {nq}x{nk} {causal} {align} s={num_splits}")
+
+
+@pytest.mark.parametrize("num_splits", [0, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_small_grid_workload(causal, num_splits):
+    """The [B=8, N=1024, D=64] bf16 workload (64 workgroups of 128 query rows),
+    with the library's split choice and with 4 splits, every output element
+    against the oracle."""
+    name = "b8h1_n1024_d64_bf16"
+    _banner(f"splitkv {name} causal={causal} splits={num_splits}")
+    w = fa_inputs.WORKLOADS[name]
+    qb, kb, vb = fa_inputs.workload_inputs(w)
+    o, lse = _run_split(qb, kb, vb, w.dtype, causal, "top-left", w.scale, num_splits)
+    o_ref, lse_ref = parity.reference_full(qb, kb, vb, w.dtype, w.scale, causal)
+    parity.check(o, lse, o_ref, lse_ref, w.dtype, f"splitkv {name} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_long_keys_sampled(causal):
+    """One query tile over 16384 keys (D = 128, bf16): the library picks 32
+    splits; sampled rows against the oracle."""
+    _banner(f"splitkv long keys causal={causal}")
+    B, H, nq, nk, D = 1, 2, 200, 16384, 128
+    assert fa.fa_splitkv_auto_splits(B, H, nq, nk, D) > 8
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, "bf16", 8080 + causal)
+    scale = parity.default_scale(D)
+    o, lse = _run_split(qb, kb, vb, "bf16", causal, "bottom-right", scale, 0)
+    rows = parity.sample_rows(B, H, nq, 80, 5)
+    q, k, v = (fa_inputs.to_f32(x, "bf16") for x in (qb, kb, vb))
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, causal, rows, causal_align="bottom-right")
+    o_s = o.reshape(B * H, nq, D)[rows[:, 0], rows[:, 1]]
+    l_s = lse.reshape(B * H, nq)[rows[:, 0], rows[:, 1]]
+    parity.check(o_s, l_s, o_ref, lse_ref, "bf16", "splitkv long keys")
+
+
+def test_splitkv_one_split_is_single_pass():
+    """num_splits = 1 runs the single-pass kernel: bit-identical to fa_fwd_ex."""
+    import torch
+    _banner("splitkv one split")
+    qb, kb, vb = fa_inputs.draw_qkv_cross(1, 3, 150, 400, 128, "bf16", 61)
+    q, k, v = (parity.to_device(x, "bf16") for x in (qb, kb, vb))
+    o1, l1 = fa.fa_fwd_ex(q, k, v, causal=True, causal_align="bottom-right")
+    o2, l2 = fa.fa_fwd_splitkv(q, k, v, causal=True, causal_align="bottom-right", num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_splitkv_workspace_reuse():
+    """Two calls in a row on one workspace, the second smaller: both correct."""
+    import torch
+    _banner("splitkv workspace reuse")
+    big = fa_inputs.draw_qkv_cross(2, 2, 256, 1000, 64, "bf16", 71)
+    small = fa_inputs.draw_qkv_cross(1, 1, 64, 300, 64, "bf16", 72)
+    need = fa.fa_fwd_splitkv_workspace_size(2, 2, 256, 1000, 64, 6)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for qb, kb, vb in (big, small):
+        q, k, v = (parity.to_device(x, "bf16") for x in (qb, kb, vb))
+        o, lse = fa.fa_fwd_splitkv(q, k, v, causal=True, num_splits=6, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = parity.reference_full_ex(qb, kb, vb, "bf16", 0.125, True, "top-left")
+        parity.check(parity.from_device(o), lse.cpu().numpy(), o_ref, lse_ref, "bf16", "reuse")
+
+
 def test_no_lse_output():
     import torch
     _banner("lse = NULL")
