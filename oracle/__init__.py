@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package. The HIP path
 never imports it and shares no code with it.
 
-Two functions:
+Functions:
 
 * :func:`attention_rows` / :func:`attention` -- the explicit definition of
   softmax attention in fp64 (C, ``attention_ref.c``): S = scale*QK^T,
@@ -14,6 +14,10 @@ Two functions:
 * :func:`oracle.tiled.tiled_attention` -- the online-softmax tile recurrence
   in fp64 (numpy), used to check that the recurrence reaches the explicit
   result.
+* :func:`attention_bwd` -- the explicit fp64 gradients dQ, dK, dV of the
+  forward for an upstream gradient dO (C, ``attention_bwd_ref.c``), in the
+  order the pages give for the FlashAttention-2 backward ("FlashAttention 2
+  from PyTorch to Triton", What is wrong with this kernel, item 5).
 
 Pins that tie these to the pages and to mathematics (not to themselves) live
 in ``tests/test_oracle.py``.
@@ -29,6 +33,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "attention_ref.c")
 LIBRARY = os.path.join(_HERE, "liboracle_attention.so")
+BWD_SOURCE = os.path.join(_HERE, "attention_bwd_ref.c")
+BWD_LIBRARY = os.path.join(_HERE, "liboracle_attention_bwd.so")
 
 # -ffp-contract=off: every product and sum is rounded on its own, as written.
 GCC_FLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11"]
@@ -39,6 +45,12 @@ def build(source: str = SOURCE, output: str = LIBRARY) -> str:
     cmd = ["gcc", *GCC_FLAGS, "-o", output, source, "-lm"]
     subprocess.run(cmd, check=True)
     return output
+
+
+def build_all() -> None:
+    """Compile the forward and backward oracles."""
+    build(SOURCE, LIBRARY)
+    build(BWD_SOURCE, BWD_LIBRARY)
 
 
 _lib_cache: dict = {}
@@ -126,3 +138,49 @@ def attention(q, k, v, scale, causal, n_kv=None, causal_align="top-left", lib_pa
                             np.asarray(v).reshape(BH, Nk, D), scale, causal, rows,
                             n_kv, causal_align, lib_path)
     return o.reshape(*lead, Nq, D), lse.reshape(*lead, Nq)
+
+
+def load_bwd(path: str = BWD_LIBRARY):
+    """Load (building if absent or stale) the backward oracle library."""
+    key = ("bwd", path)
+    if key in _lib_cache:
+        return _lib_cache[key]
+    if path == BWD_LIBRARY and (not os.path.exists(path)
+                                or os.path.getmtime(path) < os.path.getmtime(BWD_SOURCE)):
+        build(BWD_SOURCE, BWD_LIBRARY)
+    lib = ctypes.CDLL(path)
+    fn = lib.oracle_attention_bwd
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    _lib_cache[key] = lib
+    return lib
+
+
+def attention_bwd(q, k, v, dout, scale, causal, causal_align="top-left", lib_path=BWD_LIBRARY):
+    """dQ, dK, dV (fp64) of O = softmax(scale Q K^T) V for upstream gradient dout.
+
+    q, dout: float32 [..., Nq, D]; k, v: [..., Nk, D] (exact input values).
+    Returns arrays shaped like q, k and v respectively.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    lead = q.shape[:-2]
+    Nq, D = q.shape[-2:]
+    Nk = k.shape[-2]
+    BH = int(np.prod(lead)) if lead else 1
+    q3 = np.ascontiguousarray(q, dtype=np.float32).reshape(BH, Nq, D)
+    k3 = np.ascontiguousarray(k, dtype=np.float32).reshape(BH, Nk, D)
+    v3 = np.ascontiguousarray(v, dtype=np.float32).reshape(BH, Nk, D)
+    d3 = np.ascontiguousarray(dout, dtype=np.float32).reshape(BH, Nq, D)
+    dq = np.empty((BH, Nq, D), np.float64)
+    dk = np.empty((BH, Nk, D), np.float64)
+    dv = np.empty((BH, Nk, D), np.float64)
+    coff = causal_offset(Nq, Nk, causal_align)
+    rc = load_bwd(lib_path).oracle_attention_bwd(
+        q3.ctypes.data, k3.ctypes.data, v3.ctypes.data, d3.ctypes.data, BH, Nq, Nk, D,
+        float(scale), int(bool(causal)), int(coff), dq.ctypes.data, dk.ctypes.data,
+        dv.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attention_bwd failed with code {rc}")
+    return dq.reshape(*lead, Nq, D), dk.reshape(*lead, Nk, D), dv.reshape(*lead, Nk, D)

@@ -14,7 +14,7 @@ import pytest
 import fa_inputs
 import oracle
 from oracle.tiled import tiled_attention
-from tests import oracle_pins
+from tests import oracle_bwd_pins, oracle_pins
 
 
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
@@ -167,3 +167,48 @@ def test_generator_is_seeded_and_follows_recipe():
     qf = fa_inputs.to_f32(q, "bf16")
     assert 6.0 < qf.std() < 10.0
     assert math.isclose(w.scale, 1 / math.sqrt(128))
+
+
+# ---------------------------------------------------------------------------
+# Backward oracle: pins and mutants
+
+
+@pytest.mark.parametrize("pin", oracle_bwd_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_bwd_pin(pin):
+    pin()
+
+
+BWD_MUTANTS = {
+    "delta_term_dropped": ("dSi[j] = Pi[j] * (dp - Di);", "dSi[j] = Pi[j] * dp;"),
+    "delta_sign_flipped": ("dSi[j] = Pi[j] * (dp - Di);", "dSi[j] = Pi[j] * (dp + Di);"),
+    "dq_scale_dropped": ("dqh[i * D + d] = scale * acc;", "dqh[i * D + d] = acc;"),
+    "dk_uses_keys": ("acc_k += dS[i * Nk + j] * (double)qh[i * D + d];",
+                     "acc_k += dS[i * Nk + j] * (double)kh[j * D + d];"),
+    "dv_uses_ds": ("acc_v += P[i * Nk + j] * (double)doh[i * D + d];",
+                   "acc_v += dS[i * Nk + j] * (double)doh[i * D + d];"),
+    "probabilities_unnormalised": ("for (int64_t j = 0; j < n_vis; ++j) Pi[j] = exp(Pi[j] - L);",
+                                   "for (int64_t j = 0; j < n_vis; ++j) Pi[j] = exp(Pi[j] - m);"),
+    "causal_offset_dropped": ("if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;",
+                              "if (causal && i + 1 < n_vis) n_vis = i + 1;"),
+    "dp_transposed_value": ("for (int64_t d = 0; d < D; ++d) dp += (double)doi[d] * (double)vh[j * D + d];",
+                            "for (int64_t d = 0; d < D; ++d) dp += (double)doi[d] * (double)vh[d * Nk + j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(name, mutant_dir):
+    src = open(oracle.BWD_SOURCE).read()
+    old, new = BWD_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path_c = os.path.join(mutant_dir, f"bwd_{name}.c")
+    path_so = os.path.join(mutant_dir, f"libbwd_{name}.so")
+    with open(path_c, "w") as f:
+        f.write(src.replace(old, new))
+    oracle.build(path_c, path_so)
+    failed = []
+    for pin in oracle_bwd_pins.ALL_PINS:
+        try:
+            pin(lib_path=path_so)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches backward mutant {name}"
