@@ -12,6 +12,8 @@ The functions mirror the C ABI of ``include/fa.h``:
   top-left or bottom-right causal mask;
 * :func:`fa_fwd_splitkv` -- the same result for small grids, with the keys
   of every query tile split over several workgroups and combined;
+* :func:`fa_bwd` -- the backward pass: dQ, dK, dV from the forward's inputs,
+  output and log-sum-exp;
 * :func:`fa_fwd_nk` -- the same with only the first ``n_kv`` keys visible;
 * :func:`fa_fwd_variant` -- run a named kernel variant (tuning);
 * :func:`fa_num_variants`, :func:`fa_variant_name`, :func:`fa_strerror`,
@@ -38,6 +40,7 @@ SIGNATURES = {
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _I,
                             _P, ctypes.c_size_t, _P]),
+    "fa_bwd": (_I, [_P] * 10 + [_I64] * 5 + [_I, _I, _F, _I, _P]),
     "fa_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I]),
     "fa_splitkv_auto_splits": (_I, [_I64, _I64, _I64, _I64, _I64]),
     "fa_fwd_nk": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
@@ -229,6 +232,43 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, *, causal=False, causal_align="top
                             _stream_handle(q, stream))
     _check(rc)
     return o, lse
+
+
+def fa_bwd(q, k, v, o, dout, lse, *, causal=False, causal_align="top-left", scale=None,
+           dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of the forward for upstream gradient ``dout``.
+
+    ``o`` and ``lse`` are the forward's outputs for the same q, k, v, causal,
+    causal_align and scale. Returns (dq, dk, dv, delta) where delta is
+    rowsum(dout * o) in fp32. 16-bit dtypes only.
+    """
+    import torch
+    lib = load_library()
+    if causal_align not in _ALIGN:
+        raise ValueError(f"causal_align must be one of {sorted(_ALIGN)}")
+    _prepare(q, k, v, o, lse, True, same_length=False)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous() \
+            or dout.device != q.device:
+        raise ValueError("dout must be a contiguous tensor like q")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
+                or t.device != ref.device:
+            raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                    B, H, Nq, Nk, D, int(bool(causal)), _ALIGN[causal_align], float(scale),
+                    _dtype_code(q), _stream_handle(q, stream))
+    _check(rc)
+    return dq, dk, dv, delta
 
 
 def fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits=0) -> int:

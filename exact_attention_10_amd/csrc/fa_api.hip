@@ -6,6 +6,7 @@
 // library allocates no memory and keeps no state; a launch is asynchronous on
 // the caller's stream.
 #include "fa.h"
+#include "fa_bwd.hpp"
 #include "fa_combine.hpp"
 #include "fa_kernel.hpp"
 #include "fa_launch.hpp"
@@ -249,6 +250,81 @@ int launch_splitkv(const void *q, const void *k, const void *v, void *o, float *
   return FA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Backward: the dQ kernel (which also writes D = rowsum(dO * O)), then the
+// dK/dV kernel, on the caller's stream.
+
+int launch_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+               const float *lse, void *dq, void *dk, void *dv, float *delta, int64_t B, int64_t H,
+               int64_t Nq, int64_t Nk, int64_t D, int causal, int causal_align, float scale,
+               int dtype, void *stream) {
+  if (!o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
+  // q, k, v, sizes, scale, dtype and alignment of q/k/v as in the forward
+  // (dq stands in for the forward's output there)
+  int rc = validate(q, k, v, dq, nullptr, B, H, Nq, Nk, Nk, D, causal_align, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(dout) |
+                        reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(dq) |
+                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv) |
+                        reinterpret_cast<uintptr_t>(delta);
+  if (mis & 15) return FA_ERR_ALIGNMENT;
+  const int es = elem_bytes(dtype);
+  const int64_t qb = B * H * Nq * D * es, kb = B * H * Nk * D * es, lb = B * H * Nq * (int64_t)sizeof(float);
+  struct Span { const void *p; int64_t n; };
+  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {dout, qb}, {lse, lb}};
+  const Span outs[] = {{dq, qb}, {dk, kb}, {dv, kb}, {delta, lb}};
+  for (const Span &a : outs) {
+    for (const Span &b : ins)
+      if (overlaps(a.p, a.n, b.p, b.n)) return FA_ERR_INVALID_ARG;
+    for (const Span &b : outs)
+      if (&a != &b && overlaps(a.p, a.n, b.p, b.n)) return FA_ERR_INVALID_ARG;
+  }
+  const int64_t nk_tiles = (Nk + 127) / 128;
+  if (B * H > INT64_C(0x7fffffff) / nk_tiles) return FA_ERR_UNSUPPORTED;
+
+  const FaBwdLaunch L = fa_bwd_instance(dtype, (int)D, causal != 0);
+  if (!L.dq_fn || !L.dkdv_fn) return FA_ERR_UNSUPPORTED;
+  if (L.dq_lds > 65536) opt_in_lds(L.dq_fn, L.dq_lds);
+  if (L.dkdv_lds > 65536) opt_in_lds(L.dkdv_fn, L.dkdv_lds);
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.nq = Nq;
+  p.nk = Nk;
+  p.coff = causal_align == FA_CAUSAL_BOTTOM_RIGHT ? Nk - Nq : 0;
+  p.xcd_remap = 1;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.scale = scale;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  p.n_tiles = (int)((Nq + 127) / 128);
+  void *args[] = {&p};
+  hipError_t e = hipLaunchKernel(L.dq_fn, dim3((unsigned)(B * H * p.n_tiles)), dim3(256), args,
+                                 (size_t)L.dq_lds, st);
+  if (e == hipSuccess) {
+    fa::BwdParams p2 = p;
+    p2.n_tiles = (int)nk_tiles;
+    void *args2[] = {&p2};
+    e = hipLaunchKernel(L.dkdv_fn, dim3((unsigned)(B * H * p2.n_tiles)), dim3(256), args2,
+                        (size_t)L.dkdv_lds, st);
+  }
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_error, sizeof(g_hip_error), "%s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 // Kernels that use more than 64 KB of LDS raise their limit once per process.
 void opt_in_lds(const void *fn, int bytes) {
   static std::mutex mu;
@@ -309,6 +385,14 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
                    size_t workspace_bytes, void *stream) {
   return launch_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, causal, causal_align, scale, dtype,
                         num_splits, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta, int64_t B, int64_t H,
+           int64_t Nq, int64_t Nk, int64_t D, int causal, int causal_align, float scale,
+           int dtype, void *stream) {
+  return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, D, causal,
+                    causal_align, scale, dtype, stream);
 }
 
 int fa_num_variants(void) { return kNumVariants; }

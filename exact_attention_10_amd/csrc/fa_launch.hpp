@@ -21,3 +21,13 @@ FaLaunch fa_pingpong_instance(int dt, int d, bool causal);
 // split-KV: the default kernel in split mode (4 waves) and the combine kernel
 FaLaunch fa_splitkv_instance(int dt, int d, bool causal);
 const void *fa_combine_instance(int dt, int d);
+
+// backward: the dQ (and D) kernel and the dK/dV kernel, 256 threads each;
+// both null for an unsupported combination (fp32 has no backward)
+struct FaBwdLaunch {
+  const void *dq_fn;
+  int dq_lds;
+  const void *dkdv_fn;
+  int dkdv_lds;
+};
+FaBwdLaunch fa_bwd_instance(int dt, int d, bool causal);

@@ -137,6 +137,33 @@ size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq,
 int fa_splitkv_auto_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D);
 
 /*
+ * Backward pass: dQ, dK, dV of O = softmax(scale Q K^T) V for an upstream
+ * gradient dout, from the forward's inputs, its output o and its row
+ * log-sum-exp lse (natural log, as fa_fwd_ex writes it). The probabilities
+ * are recomputed tile by tile as P = exp(S - L), the row vector
+ * D = rowsum(dout * o) is formed first, the key gradients come from a kernel
+ * that walks the query tiles of each key tile, and dQ from a second pass
+ * (no atomics, deterministic): "FlashAttention 2 from PyTorch to Triton",
+ * What is wrong with this kernel, item 5. With dS = P (dout V^T - D):
+ * dV = P^T dout, dQ = scale dS K, dK = scale dS^T Q.
+ *  - q, o, dout, dq: [B,H,Nq,D]; k, v, dk, dv: [B,H,Nk,D]; all of `dtype`,
+ *    which must be FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_ERR_UNSUPPORTED for
+ *    fp32). lse: fp32 [B,H,Nq], required.
+ *  - delta: caller-owned fp32 [B,H,Nq] scratch; on return it holds D.
+ *  - causal / causal_align / scale as in fa_fwd_ex (use the forward's).
+ *  - Keys that no query sees get dK = dV = 0; query rows that see no key
+ *    (lse = -inf) get dQ = 0.
+ *  - dq, dk, dv and delta must not overlap each other or any input
+ *    (FA_ERR_INVALID_ARG); every pointer must be 16-byte aligned.
+ * Asynchronous on `stream` like the forward; allocates nothing.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+           float *delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+           int64_t D, int causal, int causal_align, float scale, int dtype,
+           void *stream);
+
+/*
  * As fa_fwd, with only the first n_kv keys (0 <= n_kv <= N) visible: keys
  * j >= n_kv are masked for every query. The query and key lengths play
  * separate roles, as "Triton: FlashAttention-2 Forward Pass" (Masks and

@@ -6,6 +6,16 @@ Tolerances (written here, used by every parity test):
   relative error is unbounded near zero outputs).
 * LSE (fp32, natural log): max |LSE_gpu - LSE_ref| <= 1e-3.
 O_ref and LSE_ref are the fp64 oracle on the same rounded inputs.
+
+Backward (dQ, dK, dV in bf16/fp16): normwise per tensor,
+max|G_gpu - G_ref| / max|G_ref| <= 1e-2 for bf16 and 3e-3 for fp16, against
+the fp64 backward oracle on the same rounded inputs. The kernels round P and
+dS to the input type before their products and the gradients once at the end
+(relative 2^-9 each for bf16, 2^-11 for fp16); sums of many terms with
+independent rounding errors keep a relative error of that order, so the bound
+leaves a margin of about 2.5x over three such roundings. D = rowsum(dO * O)
+(fp32) is checked against the same sum in fp64 over the kernel's own O,
+relative to max|D|, within 1e-5.
 """
 from __future__ import annotations
 
@@ -19,6 +29,8 @@ import oracle
 TOL_O_16 = 1e-2
 TOL_O_32_NORMWISE = 1e-5
 TOL_LSE = 1e-3
+TOL_GRAD = {"bf16": 1e-2, "fp16": 3e-3}
+TOL_DELTA = 1e-5
 
 
 def torch_dtype(dtype):
@@ -104,3 +116,15 @@ def reference_rows(q_bits, k_bits, v_bits, dtype, scale, causal, rows, n_kv=None
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+def check_grad(g_gpu, g_ref, dtype, what=""):
+    """Normwise parity of one gradient tensor; returns the error."""
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    assert np.isfinite(g_gpu).all(), f"{what}: non-finite gradient"
+    ref_max = np.abs(g_ref).max() if g_ref.size else 0.0
+    diff = np.abs(g_gpu - g_ref).max() if g_ref.size else 0.0
+    err = diff / ref_max if ref_max > 0 else diff
+    assert err <= TOL_GRAD[dtype], f"{what}: normwise gradient error {err:.3e}"
+    return err

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+    for n in ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
               "fa_splitkv_auto_splits", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
               "fa_num_variants", "fa_variant_name"):
         assert n in names
@@ -174,6 +174,39 @@ def test_splitkv_auto_choice(lib):
 ])
 def test_splitkv_validation(lib, kw, code):
     assert call_split(lib, **kw) == code
+
+
+# fake addresses for the backward's extra tensors: [2,4,256,128] bf16 = 512 KiB each
+OO, DO, DQ, DK, DV, DL = 0x90000000, 0xA0000000, 0xB0000000, 0xC0000000, 0xD0000000, 0xE0000000
+
+
+def call_bwd(lib, q=Q, k=K, v=V, o=OO, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, H=4,
+             Nq=256, Nk=256, D=128, causal=1, align=fa.FA_CAUSAL_TOP_LEFT, scale=0.088,
+             dtype=fa.FA_DTYPE_BF16):
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, B, H, Nq, Nk, D, causal, align,
+                      scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(delta=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(do=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_DTYPE_FP32), fa.FA_ERR_UNSUPPORTED),     # no fp32 backward
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(align=3), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=Q), fa.FA_ERR_INVALID_ARG),                         # output aliases an input
+    (dict(dk=DV), fa.FA_ERR_INVALID_ARG),                        # two outputs alias
+    (dict(dv=DO + 4096), fa.FA_ERR_INVALID_ARG),                 # output inside dout
+    (dict(delta=L + 64), fa.FA_ERR_INVALID_ARG),                 # delta inside lse
+    (dict(delta=DL + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(do=DO + 8), fa.FA_ERR_ALIGNMENT),
+])
+def test_bwd_validation(lib, kw, code):
+    assert call_bwd(lib, **kw) == code
 
 
 def test_lse_may_be_null_for_validation(lib):

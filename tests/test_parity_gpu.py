@@ -280,6 +280,74 @@ def test_splitkv_workspace_reuse():
         parity.check(parity.from_device(o), lse.cpu().numpy(), o_ref, lse_ref, "bf16", "reuse")
 
 
+# ---------------------------------------------------------------------------
+# Backward (fa_bwd) against the fp64 backward oracle
+
+
+def _run_fwd_bwd(qb, kb, vb, dob, dtype, causal, align, scale):
+    import torch
+    q, k, v, do = (parity.to_device(x, dtype) for x in (qb, kb, vb, dob))
+    o, lse = fa.fa_fwd_ex(q, k, v, causal=causal, causal_align=align, scale=scale)
+    dq, dk, dv, delta = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, causal_align=align,
+                                  scale=scale)
+    torch.cuda.synchronize()
+    return (parity.from_device(dq), parity.from_device(dk), parity.from_device(dv),
+            delta.cpu().numpy(), parity.from_device(o))
+
+
+BWD_SHAPES = [(64, 64), (130, 130), (37, 200), (200, 37), (1, 65), (128, 300), (257, 511)]
+
+
+@pytest.mark.parametrize("causal,align", MASKS)
+@pytest.mark.parametrize("nq,nk", BWD_SHAPES)
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp16", 128), ("fp16", 64)])
+def test_bwd_parity(dtype, D, nq, nk, causal, align):
+    _banner(f"bwd dtype={dtype} D={D} Nq={nq} Nk={nk} causal={causal} {align}")
+    B, H = 2, 2
+    seed = 7000 + nq * 3 + nk + D + (1 if dtype == "fp16" else 0) + (5 if causal else 0) \
+        + (9 if align == "bottom-right" else 0)
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, dtype, seed)
+    dob = fa_inputs.draw_qkv_cross(B, H, nq, 1, D, dtype, seed + 1)[0]
+    scale = parity.default_scale(D)
+    dq, dk, dv, delta, o = _run_fwd_bwd(qb, kb, vb, dob, dtype, causal, align, scale)
+    q, k, v, do = (fa_inputs.to_f32(x, dtype) for x in (qb, kb, vb, dob))
+    dq_r, dk_r, dv_r = oracle.attention_bwd(q, k, v, do, scale, causal, align)
+    what = f"bwd {dtype} D={D} {nq}x{nk} {causal} {align}"
+    errs = [parity.check_grad(g, r, dtype, f"{what} {n}")
+            for n, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r))]
+    d_ref = (do.astype(np.float64) * o.astype(np.float64)).sum(-1)
+    d_err = np.abs(delta - d_ref).max() / max(1e-30, np.abs(d_ref).max())
+    print(f"[bwd errors] {what}: dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e} D {d_err:.2e}",
+          flush=True)
+    assert d_err <= parity.TOL_DELTA, f"{what}: D error {d_err:.3e}"
+
+
+def test_bwd_unseen_keys_and_rows_are_zero():
+    """Top-left causal with more keys than queries: keys j >= Nq are seen by no
+    query, so dK and dV are exactly 0 there; bottom-right with more queries
+    than keys: rows i < Nq - Nk see no key and get dQ = 0 exactly."""
+    import torch
+    _banner("bwd unseen keys / rows")
+    for nq, nk, align in ((100, 300, "top-left"), (300, 100, "bottom-right")):
+        qb, kb, vb = fa_inputs.draw_qkv_cross(1, 2, nq, nk, 128, "bf16", 91)
+        dob = fa_inputs.draw_qkv_cross(1, 2, nq, 1, 128, "bf16", 92)[0]
+        dq, dk, dv, _, _ = _run_fwd_bwd(qb, kb, vb, dob, "bf16", True, align, 128 ** -0.5)
+        if nk > nq:
+            assert (dk[:, :, nq:] == 0).all() and (dv[:, :, nq:] == 0).all()
+        else:
+            assert (dq[:, :, : nq - nk] == 0).all()
+
+
+def test_bwd_bitwise_deterministic():
+    import torch
+    _banner("bwd determinism")
+    qb, kb, vb = fa_inputs.draw_qkv_cross(2, 4, 300, 300, 128, "bf16", 93)
+    dob = fa_inputs.draw_qkv_cross(2, 4, 300, 1, 128, "bf16", 94)[0]
+    r1 = _run_fwd_bwd(qb, kb, vb, dob, "bf16", True, "top-left", 128 ** -0.5)
+    r2 = _run_fwd_bwd(qb, kb, vb, dob, "bf16", True, "top-left", 128 ** -0.5)
+    assert all(np.array_equal(a, b) for a, b in zip(r1, r2))
+
+
 def test_no_lse_output():
     import torch
     _banner("lse = NULL")
