@@ -133,6 +133,35 @@ def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False):
             "flops": flops}
 
 
+def time_bwd(w, causal, steps, warmup, torch, fa):
+    """Backward timing: the forward runs once untimed for O and LSE, then
+    `warmup` + `steps` fa_bwd calls, timed like time_gpu."""
+    (q, k, v), _ = _device_inputs(w, torch)
+    g = torch.Generator(device=q.device)
+    g.manual_seed(w.seed + 1000)
+    dout = torch.randn(q.shape, device=q.device, generator=g).to(q.dtype)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.fa_bwd(q, k, v, o, dout, lse, causal=causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                  delta=delta, stream=stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = 2.5 * attention_flops(w.B, w.H, w.N, w.D, causal)
+    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def cpu_baseline(w, causal, target_s=15.0):
     """The fp64 oracle on a bounded sample of rows of the same workload."""
     import oracle
@@ -163,8 +192,8 @@ def cpu_baseline(w, causal, target_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=fa_inputs.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -248,6 +277,17 @@ def main():
                             small.B, small.H, small.N, small.N, small.D)
                     print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s",
                           file=sys.stderr, flush=True)
+
+        # the backward at the headline shape (fa_bwd: dQ kernel then dK/dV
+        # kernel), FLOPs counted as 2.5x the forward's (five N x N x D products)
+        for causal in (False, True):
+            r = time_bwd(w, causal, max(10, a.steps // 2), max(5, a.warmup // 2), torch, fa)
+            key = f"{w.name}_{'causal' if causal else 'noncausal'}_backward"
+            extra[key] = {"ms": round(r["ms"], 5), "tflops": round(r["tflops"], 2),
+                          "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                          "flops_counted": "2.5x forward"}
+            print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
 
     esize = fa_inputs.ESIZE[w.dtype]
     roofline = {
