@@ -18,6 +18,9 @@ Functions:
   forward for an upstream gradient dO (C, ``attention_bwd_ref.c``), in the
   order the pages give for the FlashAttention-2 backward ("FlashAttention 2
   from PyTorch to Triton", What is wrong with this kernel, item 5).
+* :func:`attention_bwd_sampled` -- the same gradients for one head on
+  selected query rows (dQ) and key rows (dK, dV) only, evaluated element by
+  element so that single outputs of a long sequence can be checked.
 
 Pins that tie these to the pages and to mathematics (not to themselves) live
 in ``tests/test_oracle.py``.
@@ -153,6 +156,11 @@ def load_bwd(path: str = BWD_LIBRARY):
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    fs = lib.oracle_attention_bwd_sampled
+    fs.restype = ctypes.c_int
+    fs.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3
     _lib_cache[key] = lib
     return lib
 
@@ -184,3 +192,35 @@ def attention_bwd(q, k, v, dout, scale, causal, causal_align="top-left", lib_pat
     if rc != 0:
         raise ValueError(f"oracle_attention_bwd failed with code {rc}")
     return dq.reshape(*lead, Nq, D), dk.reshape(*lead, Nk, D), dv.reshape(*lead, Nk, D)
+
+
+def attention_bwd_sampled(q, k, v, dout, scale, causal, rows, cols, causal_align="top-left",
+                          lib_path=BWD_LIBRARY):
+    """Selected outputs of the fp64 gradients for ONE head: dQ at query rows
+    ``rows`` and dK, dV at key rows ``cols`` (the definition evaluated element
+    by element, ``oracle_attention_bwd_sampled``).
+
+    q, dout: float32 [Nq, D]; k, v: [Nk, D]. Returns (dq [len(rows), D],
+    dk [len(cols), D], dv [len(cols), D]) in float64.
+    """
+    q2 = np.ascontiguousarray(q, dtype=np.float32)
+    k2 = np.ascontiguousarray(k, dtype=np.float32)
+    v2 = np.ascontiguousarray(v, dtype=np.float32)
+    d2 = np.ascontiguousarray(dout, dtype=np.float32)
+    if q2.ndim != 2 or k2.shape != v2.shape or d2.shape != q2.shape or k2.shape[1] != q2.shape[1]:
+        raise ValueError("attention_bwd_sampled takes one head: q, dout [Nq, D] and k, v [Nk, D]")
+    Nq, D = q2.shape
+    Nk = k2.shape[0]
+    r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    c = np.ascontiguousarray(cols, dtype=np.int64).reshape(-1)
+    dq = np.empty((len(r), D), np.float64)
+    dk = np.empty((len(c), D), np.float64)
+    dv = np.empty((len(c), D), np.float64)
+    rc = load_bwd(lib_path).oracle_attention_bwd_sampled(
+        q2.ctypes.data, k2.ctypes.data, v2.ctypes.data, d2.ctypes.data, Nq, Nk, D,
+        float(scale), int(bool(causal)), int(causal_offset(Nq, Nk, causal_align)),
+        r.ctypes.data, len(r), c.ctypes.data, len(c), dq.ctypes.data, dk.ctypes.data,
+        dv.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attention_bwd_sampled failed with code {rc}")
+    return dq, dk, dv

@@ -114,3 +114,135 @@ int oracle_attention_bwd(const float *q, const float *k, const float *v, const f
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * The same gradients for one head, on selected outputs only: dQ for the query
+ * rows rows[0..n_rows) and dK, dV for the key rows cols[0..n_cols). This is
+ * the definition above evaluated element by element, so that single outputs
+ * of a long sequence can be checked without the Nq x Nk matrices:
+ *   - L_i and D_i are computed for every query row first (steps 1-3);
+ *   - dQ_r = scale * sum_j P_rj (dP_rj - D_r) k_j, over visible j ascending;
+ *   - dV_c = sum_i P_ic dO_i and dK_c = scale * sum_i P_ic (dP_ic - D_i) q_i,
+ *     over the query rows i that see key c, ascending.
+ * Layout: q, dout [Nq][D]; k, v [Nk][D]; dq_rows [n_rows][D];
+ * dk_cols, dv_cols [n_cols][D] (double). Rows and columns run in parallel;
+ * every sum is sequential.
+ */
+int oracle_attention_bwd_sampled(const float *q, const float *k, const float *v,
+                                 const float *dout, int64_t Nq, int64_t Nk, int64_t D,
+                                 double scale, int causal, int64_t coff,
+                                 const int64_t *rows, int64_t n_rows,
+                                 const int64_t *cols, int64_t n_cols,
+                                 double *dq_rows, double *dk_cols, double *dv_cols)
+{
+    if (!q || !k || !v || !dout) return -1;
+    if (Nq < 1 || Nk < 1 || D < 1 || n_rows < 0 || n_cols < 0) return -1;
+    if ((n_rows && (!rows || !dq_rows)) || (n_cols && (!cols || !dk_cols || !dv_cols)))
+        return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= Nq) return -1;
+    for (int64_t c = 0; c < n_cols; ++c)
+        if (cols[c] < 0 || cols[c] >= Nk) return -1;
+
+    double *L = (double *)malloc(sizeof(double) * (size_t)Nq);
+    double *Dv = (double *)malloc(sizeof(double) * (size_t)Nq);
+    if (!L || !Dv) {
+        free(L);
+        free(Dv);
+        return -2;
+    }
+    int failed = 0;
+
+    /* steps 1-3 for every row: L_i, and D_i from O_i */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < Nq; ++i) {
+        int64_t n_vis = Nk;
+        if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;
+        L[i] = -INFINITY;
+        Dv[i] = 0.0;
+        if (n_vis <= 0) continue;
+        double *s = (double *)malloc(sizeof(double) * (size_t)n_vis);
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !o) {
+#pragma omp atomic write
+            failed = 1;
+            free(s);
+            free(o);
+            continue;
+        }
+        const float *qi = q + i * D;
+        for (int64_t j = 0; j < n_vis; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)k[j * D + d];
+            s[j] = scale * dot;
+        }
+        double m = s[0];
+        for (int64_t j = 1; j < n_vis; ++j)
+            if (s[j] > m) m = s[j];
+        double l = 0.0;
+        for (int64_t j = 0; j < n_vis; ++j) l += exp(s[j] - m);
+        const double Li = m + log(l);
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int64_t j = 0; j < n_vis; ++j) {
+            const double p = exp(s[j] - Li);
+            for (int64_t d = 0; d < D; ++d) o[d] += p * (double)v[j * D + d];
+        }
+        const float *doi = dout + i * D;
+        double Di = 0.0;
+        for (int64_t d = 0; d < D; ++d) Di += (double)doi[d] * o[d];
+        L[i] = Li;
+        Dv[i] = Di;
+        free(s);
+        free(o);
+    }
+    if (failed) {
+        free(L);
+        free(Dv);
+        return -2;
+    }
+
+    /* dQ of the selected rows */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t i = rows[r];
+        int64_t n_vis = Nk;
+        if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;
+        double *out = dq_rows + r * D;
+        for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+        const float *qi = q + i * D, *doi = dout + i * D;
+        for (int64_t j = 0; j < n_vis; ++j) {
+            double dot = 0.0, dp = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)k[j * D + d];
+            for (int64_t d = 0; d < D; ++d) dp += (double)doi[d] * (double)v[j * D + d];
+            const double ds = exp(scale * dot - L[i]) * (dp - Dv[i]);
+            for (int64_t d = 0; d < D; ++d) out[d] += ds * (double)k[j * D + d];
+        }
+        for (int64_t d = 0; d < D; ++d) out[d] *= scale;
+    }
+
+    /* dK and dV of the selected keys */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < n_cols; ++c) {
+        const int64_t j = cols[c];
+        double *ok = dk_cols + c * D, *ov = dv_cols + c * D;
+        for (int64_t d = 0; d < D; ++d) ok[d] = 0.0, ov[d] = 0.0;
+        const float *kj = k + j * D, *vj = v + j * D;
+        for (int64_t i = 0; i < Nq; ++i) {
+            if (causal && j > i + coff) continue;   /* key j is in row i's future */
+            const float *qi = q + i * D, *doi = dout + i * D;
+            double dot = 0.0, dp = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qi[d] * (double)kj[d];
+            for (int64_t d = 0; d < D; ++d) dp += (double)doi[d] * (double)vj[d];
+            const double p = exp(scale * dot - L[i]);
+            const double ds = p * (dp - Dv[i]);
+            for (int64_t d = 0; d < D; ++d) {
+                ov[d] += p * (double)doi[d];
+                ok[d] += ds * (double)qi[d];
+            }
+        }
+        for (int64_t d = 0; d < D; ++d) ok[d] *= scale;
+    }
+    free(L);
+    free(Dv);
+    return 0;
+}

@@ -103,5 +103,55 @@ def pin_unseen_rows_and_keys(lib_path=oracle.BWD_LIBRARY):
     assert (dk[0, 3:] == 0).all() and (dv[0, 3:] == 0).all()
 
 
+def pin_sampled_finite_differences(lib_path=oracle.BWD_LIBRARY):
+    """The single-head, selected-output gradients (attention_bwd_sampled)
+    against central differences of the forward oracle's sum(dO * O), for
+    chosen elements of the selected rows of Q and key rows of K and V, under
+    no mask and under causal masks of both alignments."""
+    cases = [((7, 9, 4), False, "top-left"), ((9, 6, 3), True, "bottom-right"),
+             ((8, 8, 5), True, "top-left")]
+    for c, ((nq, nk, D), causal, align) in enumerate(cases):
+        q, k, v = _rand((nq, D), 400 + c), _rand((nk, D), 410 + c), _rand((nk, D), 420 + c)
+        dout = _rand((nq, D), 430 + c)
+        scale = 0.6
+        rows, cols = np.array([0, nq // 2, nq - 1]), np.array([0, nk // 3, nk - 1])
+        dq, dk, dv = oracle.attention_bwd_sampled(q, k, v, dout, scale, causal, rows, cols,
+                                                  causal_align=align, lib_path=lib_path)
+        rng = np.random.default_rng(440 + c)
+        for name, x, sel, g in (("Q", q, rows, dq), ("K", k, cols, dk), ("V", v, cols, dv)):
+            for r in range(len(sel)):
+                d = int(rng.integers(0, D))
+                idx = (int(sel[r]), d)
+                h = np.float32(2.0 ** -8)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args = {"Q": (xp, k, v), "K": (q, xp, v), "V": (q, k, xp)}[name]
+                argm = {"Q": (xm, k, v), "K": (q, xm, v), "V": (q, k, xm)}[name]
+                fd = (_loss(*args, dout, scale, causal, align) - _loss(*argm, dout, scale, causal, align)) \
+                    / (float(xp[idx]) - float(xm[idx]))
+                err = abs(fd - g[r, d])
+                assert err <= 2e-5 * max(1.0, abs(g[r, d])), \
+                    f"sampled d{name}{idx} case {c}: oracle {g[r, d]:.9g} vs finite difference {fd:.9g}"
+
+
+def pin_sampled_matches_full(lib_path=oracle.BWD_LIBRARY):
+    """The selected-output gradients equal the corresponding rows of the full
+    explicit gradients (two separately written evaluations of one
+    definition), including rows that see no key and keys no row sees."""
+    for nq, nk, causal, align in ((23, 31, False, "top-left"), (30, 17, True, "bottom-right"),
+                                  (19, 40, True, "top-left"), (1, 5, True, "bottom-right")):
+        q, k, v, dout = _rand((nq, 8), 450), _rand((nk, 8), 451), _rand((nk, 8), 452), _rand((nq, 8), 453)
+        dq, dk, dv = oracle.attention_bwd(q[None], k[None], v[None], dout[None], 0.45, causal, align,
+                                          lib_path=lib_path)
+        rows, cols = np.arange(nq), np.arange(nk)
+        sq, sk, sv = oracle.attention_bwd_sampled(q, k, v, dout, 0.45, causal, rows, cols,
+                                                  causal_align=align, lib_path=lib_path)
+        for what, a, b in (("dQ", sq, dq[0]), ("dK", sk, dk[0]), ("dV", sv, dv[0])):
+            assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max()), \
+                f"{what} {nq}x{nk} causal={causal} {align}: sampled and full gradients differ"
+
+
 ALL_PINS = [pin_finite_differences, pin_key_gradients_sum_to_zero, pin_single_key,
-            pin_zero_upstream, pin_constant_values, pin_unseen_rows_and_keys]
+            pin_zero_upstream, pin_constant_values, pin_unseen_rows_and_keys,
+            pin_sampled_finite_differences, pin_sampled_matches_full]

@@ -188,10 +188,17 @@ BWD_MUTANTS = {
                    "acc_v += dS[i * Nk + j] * (double)doh[i * D + d];"),
     "probabilities_unnormalised": ("for (int64_t j = 0; j < n_vis; ++j) Pi[j] = exp(Pi[j] - L);",
                                    "for (int64_t j = 0; j < n_vis; ++j) Pi[j] = exp(Pi[j] - m);"),
-    "causal_offset_dropped": ("if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;",
-                              "if (causal && i + 1 < n_vis) n_vis = i + 1;"),
+    "causal_offset_dropped": ("if (causal && i + coff + 1 < n_vis) n_vis = i + coff + 1;\n"
+                              "            double *Pi = P + i * Nk",
+                              "if (causal && i + 1 < n_vis) n_vis = i + 1;\n"
+                              "            double *Pi = P + i * Nk"),
     "dp_transposed_value": ("for (int64_t d = 0; d < D; ++d) dp += (double)doi[d] * (double)vh[j * D + d];",
                             "for (int64_t d = 0; d < D; ++d) dp += (double)doi[d] * (double)vh[d * Nk + j];"),
+    "sampled_dk_scale_dropped": ("for (int64_t d = 0; d < D; ++d) ok[d] *= scale;", ""),
+    "sampled_future_rows_kept": ("if (causal && j > i + coff) continue;", "if (causal && j > i) continue;"),
+    "sampled_dv_uses_ds": ("ov[d] += p * (double)doi[d];", "ov[d] += ds * (double)doi[d];"),
+    "sampled_dq_delta_dropped": ("const double ds = exp(scale * dot - L[i]) * (dp - Dv[i]);",
+                                 "const double ds = exp(scale * dot - L[i]) * dp;"),
 }
 
 

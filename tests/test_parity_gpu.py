@@ -338,6 +338,39 @@ def test_bwd_unseen_keys_and_rows_are_zero():
             assert (dq[:, :, : nq - nk] == 0).all()
 
 
+BWD_FULL_SIZE = [(fa_inputs.HEADLINE, False), (fa_inputs.HEADLINE, True),
+                 ("b2h16_n4000_d128_fp16", False), ("b2h16_n4000_d128_fp16", True)]
+
+
+@pytest.mark.parametrize("name,causal", BWD_FULL_SIZE,
+                         ids=[f"{n}-{'causal' if c else 'full'}" for n, c in BWD_FULL_SIZE])
+def test_bwd_full_size_sampled(name, causal):
+    """The backward at a workload's full size, in the launch configuration the
+    benchmark times (fa_fwd then fa_bwd over the whole batch): dQ on sampled
+    query rows and dK, dV on sampled key rows of three heads, against the
+    oracle's element-by-element gradients of those heads."""
+    w = fa_inputs.WORKLOADS[name]
+    _banner(f"bwd full size {name} causal={causal}")
+    qb, kb, vb = fa_inputs.workload_inputs(w)
+    dob = fa_inputs.draw_qkv_cross(w.B, w.H, w.N, 1, w.D, w.dtype, w.seed + 1000)[0]
+    dq, dk, dv, _, _ = _run_fwd_bwd(qb, kb, vb, dob, w.dtype, causal, "top-left", w.scale)
+    rng = np.random.default_rng(w.seed + 2000)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))]
+    edge = np.array([0, 1, 63, 64, 127, 128, w.N - 65, w.N - 64, w.N - 1])
+    for b, h in heads:
+        rows = np.unique(np.concatenate([edge, rng.integers(0, w.N, 24)]))
+        cols = np.unique(np.concatenate([edge, rng.integers(0, w.N, 24)]))
+        q, k, v, do = (fa_inputs.to_f32(x[b, h], w.dtype) for x in (qb, kb, vb, dob))
+        dq_r, dk_r, dv_r = oracle.attention_bwd_sampled(q, k, v, do, w.scale, causal, rows, cols)
+        what = f"bwd {name} causal={causal} head ({b},{h})"
+        errs = [parity.check_grad(g, r, w.dtype, f"{what} {n}")
+                for n, g, r in (("dQ", dq[b, h, rows], dq_r), ("dK", dk[b, h, cols], dk_r),
+                                ("dV", dv[b, h, cols], dv_r))]
+        print(f"[bwd full size] {what}: dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}",
+              flush=True)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
 def test_bwd_bitwise_deterministic():
     import torch
     _banner("bwd determinism")
