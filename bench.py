@@ -7,7 +7,11 @@ one JSON line: attention TFLOP/s (4*B*H*N^2*D FLOPs, halved for causal, the
 count of "FlashAttention 2 from PyTorch to Triton", Step 4), the fraction of
 the MI355X dense bf16 MFMA peak, the same figures for the causal mask and the
 other N=4096 workload in "extra", and the fp64 CPU oracle timed on a bounded
-sample of the same workload as "cpu_baseline".
+sample of the same workload as "cpu_baseline". "extra" also holds per-launch
+percentiles (back to back, and with the caches scrubbed before each call),
+the split-KV and backward timings; "clock" holds the graphics clock and
+socket power read while the headline call runs back to back, and the
+roofline adds the fraction of the peak scaled to that clock.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -131,6 +135,123 @@ def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False):
     flops = attention_flops(w.B, w.H, w.N, w.D, causal)
     return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,
             "flops": flops}
+
+
+class ClockSampler:
+    """Reads the GPU's graphics clock (MHz, mean over its XCDs) and socket
+    power from amdsmi's GPU metrics in a background thread. The metrics table
+    refreshes about once a second, so a reading needs a window of sustained
+    load of a few seconds (measure_clock). Reports nothing (None) where
+    amdsmi or the device's metrics are not available."""
+
+    def __init__(self, torch, period_s=0.05):
+        self.period = period_s
+        self.samples = []
+        self.handle = None
+        self._stop = None
+        self._thread = None
+        self._t0 = 0.0
+        try:
+            import amdsmi
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            amdsmi.amdsmi_init()
+            for h in amdsmi.amdsmi_get_processor_handles():
+                dom, bus, _ = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if int(bus, 16) == props.pci_bus_id and int(dom, 16) == props.pci_domain_id:
+                    self.handle = h
+            self._smi = amdsmi
+        except Exception:
+            self.handle = None
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+            clks = [m["current_gfxclk"]]
+        power = m.get("current_socket_power")
+        return (time.perf_counter() - self._t0, sum(clks) / len(clks) if clks else None,
+                power if isinstance(power, (int, float)) else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self._t0 = time.perf_counter()
+        if self.handle is not None:
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+
+def measure_clock(w, torch, fa, seconds=3.0, settle_s=1.2):
+    """The graphics clock and socket power while the headline call runs back
+    to back for `seconds`: the median of the readings taken after `settle_s`
+    (the metrics refresh about once a second). None where unavailable."""
+    (q, k, v), _ = _device_inputs(w, torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    sampler = ClockSampler(torch)
+    if sampler.handle is None:
+        return None
+    with sampler:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(200):
+                fa.fa_fwd(q, k, v, o, lse, causal=False, scale=w.scale)
+            torch.cuda.synchronize()
+    late = [(c, p) for t, c, p in sampler.samples if t >= settle_s and c is not None]
+    if not late:
+        return None
+    clk = sorted(c for c, _ in late)
+    pw = sorted(p for _, p in late if p is not None)
+    return {"sclk_mhz_median": round(clk[len(clk) // 2], 1), "sclk_mhz_min": round(clk[0], 1),
+            "sclk_mhz_max": round(clk[-1], 1), "readings": len(clk),
+            "socket_power_w_median": pw[len(pw) // 2] if pw else None,
+            "source": f"amdsmi GPU metrics (graphics clock averaged over the XCDs), read every "
+                      f"{sampler.period * 1e3:.0f} ms while {w.name} non-causal ran back to back for "
+                      f"{seconds:.0f} s, readings after the first {settle_s:.1f} s"}
+
+
+def time_per_launch(w, causal, reps, torch, fa, scrub_mib=0):
+    """Per-launch durations (median, p10, p90 in ms) from one event pair
+    around each fa_fwd call; with scrub_mib > 0 each call is preceded by an
+    untimed write of that many MiB, so that K and V start outside the L2 and
+    the memory-side cache."""
+    (q, k, v), _ = _device_inputs(w, torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    scrub = (torch.empty(scrub_mib << 18, dtype=torch.float32, device=q.device)
+             if scrub_mib else None)
+    for _ in range(10):
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+    for e0, e1 in events:
+        if scrub is not None:
+            scrub.fill_(1.0)
+        e0.record(stream)
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in events)
+    pick = lambda f: ms[min(len(ms) - 1, int(f * len(ms)))]   # noqa: E731
+    return {"median_ms": round(pick(0.5), 5), "p10_ms": round(pick(0.1), 5),
+            "p90_ms": round(pick(0.9), 5), "reps": reps,
+            "scrub_mib": scrub_mib}
 
 
 def time_bwd(w, causal, steps, warmup, torch, fa):
@@ -278,6 +399,16 @@ def main():
                     print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s",
                           file=sys.stderr, flush=True)
 
+        # per-launch distribution of the headline call, back to back and with
+        # the caches scrubbed before each call (512 MiB written, untimed)
+        for scrub in (0, 512):
+            r = time_per_launch(w, False, max(20, a.steps), torch, fa, scrub_mib=scrub)
+            r["tflops_at_median"] = round(head["flops"] / (r["median_ms"] * 1e-3) / 1e12, 2)
+            key = f"{w.name}_noncausal_per_launch{'_scrubbed' if scrub else ''}"
+            extra[key] = r
+            print(f"[bench] {key}: median {r['median_ms']:.4f} ms (p10 {r['p10_ms']:.4f}, "
+                  f"p90 {r['p90_ms']:.4f})", file=sys.stderr, flush=True)
+
         # the backward at the headline shape (fa_bwd: dQ kernel then dK/dV
         # kernel), FLOPs counted as 2.5x the forward's (five N x N x D products)
         for causal in (False, True):
@@ -288,6 +419,11 @@ def main():
                           "flops_counted": "2.5x forward"}
             print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
                   flush=True)
+
+    clock_summary = measure_clock(w, torch, fa) if not a.no_extra else None
+    if clock_summary is not None:
+        print(f"[bench] graphics clock under sustained load: {clock_summary['sclk_mhz_median']} MHz, "
+              f"{clock_summary['socket_power_w_median']} W", file=sys.stderr, flush=True)
 
     esize = fa_inputs.ESIZE[w.dtype]
     roofline = {
@@ -301,6 +437,11 @@ def main():
         "algorithmic_bytes_per_launch": attention_bytes(w.B, w.H, w.N, w.D, esize),
         "kernel": "fa_fwd_kernel<bf16, D=128, non-causal>",
     }
+    if clock_summary is not None:
+        # the same fraction against the peak scaled to the clock the GPU ran at
+        roofline["sclk_mhz_measured"] = clock_summary["sclk_mhz_median"]
+        roofline["frac_at_measured_sclk"] = round(
+            head["tflops"] / (PEAK_BF16_TFLOPS * clock_summary["sclk_mhz_median"] / 2400.0), 4)
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(w, False)
@@ -325,6 +466,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "clock": clock_summary,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
