@@ -13,7 +13,8 @@ the split-KV and backward timings; "clock" holds the graphics clock and
 socket power read while the headline call runs back to back, and the
 roofline adds the fraction of the peak scaled to that clock.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                       [--no-clock]
 """
 from __future__ import annotations
 
@@ -64,6 +65,8 @@ def kernel_sources_digest():
         with open(path, "rb") as f:
             h.update(f.read())
     h.update(" ".join(fa_build.HIPCC_FLAGS).encode())
+    for name in sorted(fa_build.FILE_FLAGS):
+        h.update((name + " " + " ".join(fa_build.FILE_FLAGS[name])).encode())
     return h.hexdigest()
 
 
@@ -318,6 +321,8 @@ def main():
     ap.add_argument("--workload", default=fa_inputs.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 3 s clock reading under sustained load")
     ap.add_argument("--sweep-variants", action="store_true",
                     help="time every kernel variant on the N=4096 workloads and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -420,7 +425,7 @@ def main():
             print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
                   flush=True)
 
-    clock_summary = measure_clock(w, torch, fa) if not a.no_extra else None
+    clock_summary = measure_clock(w, torch, fa) if not a.no_clock else None
     if clock_summary is not None:
         print(f"[bench] graphics clock under sustained load: {clock_summary['sclk_mhz_median']} MHz, "
               f"{clock_summary['socket_power_w_median']} W", file=sys.stderr, flush=True)

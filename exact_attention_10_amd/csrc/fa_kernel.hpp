@@ -344,10 +344,17 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     constexpr int buf = decltype(buf_c)::value;
     wait_vmem();
     __syncthreads();                        // tile t visible; the other buffer is free
-    if (t + 1 < t_end) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
+    // the next tile's loads go out after this tile's S MFMAs have been issued,
+    // so that they do not hold up the wave's first LDS reads and MFMAs
+    auto prefetch = [&]() __attribute__((always_inline)) {
+      if (t + 1 < t_end) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
+    };
 
     const int kstart = t * BN;
-    if (CAUSAL && kstart > qw + 31 + coff) return;   // every key of this tile is in this wave's future
+    if (CAUSAL && kstart > qw + 31 + coff) {   // every key of this tile is in this wave's future
+      prefetch();
+      return;
+    }
 
     const char *kl = smem + buf * (2 * C::TILE_BYTES);
     const char *vl = kl + C::TILE_BYTES;
@@ -406,6 +413,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
           }
       __builtin_amdgcn_sched_barrier(0);
     }
+    prefetch();
 
     // ---- masks: only on tiles past the end of the keys or on the diagonal ----
     const bool need_mask = (kstart + BN > n_kv) || (CAUSAL && kstart + BN - 1 > qw + coff);
