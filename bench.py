@@ -54,19 +54,25 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_kernel_bf16_d128_b4h16_n4096_hbm_traffic.txt")
 
 
+# the sources that make up the headline forward kernel and its launch
+FORWARD_SOURCES = ("fa_kernel.hpp", "fa_inst_simple_bf16.hip", "fa_launch.hpp", "fa_api.hip", "fa.h")
+
+
 def kernel_sources_digest():
-    """sha256 over the HIP sources and build flags of the library, so a stored
-    counter reading is only used for the kernel it was taken on."""
+    """sha256 over the sources and build flags of the headline forward kernel,
+    so a stored counter reading is only used for the kernel it was taken on."""
     import hashlib
     from exact_attention_10_amd import build as fa_build
     h = hashlib.sha256()
     for path in sorted(fa_build.DEPENDS):
-        h.update(os.path.basename(path).encode())
+        name = os.path.basename(path)
+        if name not in FORWARD_SOURCES:
+            continue
+        h.update(name.encode())
         with open(path, "rb") as f:
             h.update(f.read())
+        h.update(" ".join(fa_build.FILE_FLAGS.get(name, [])).encode())
     h.update(" ".join(fa_build.HIPCC_FLAGS).encode())
-    for name in sorted(fa_build.FILE_FLAGS):
-        h.update((name + " " + " ".join(fa_build.FILE_FLAGS[name])).encode())
     return h.hexdigest()
 
 

@@ -315,7 +315,8 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int BKEYS = 128, NQB = BQ / 32, NPC = BQ / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int bid = remap_block(blockIdx.x, gridDim.x, p.xcd_remap);
   const int bh = bid / p.n_tiles;
   const int kt = bid - bh * p.n_tiles;
@@ -352,7 +353,13 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
     const int row = lds_off / RB;
     dma_off[u] = (uint32_t)row * RB + (((lds_off % RB) / 16) ^ swz<RB>(row)) * 16;
   }
-  // stage layout: Q tile, dO tile, L (64 floats), D (64 floats)
+  // stage layout: Q tile, dO tile, the exponent offsets -L log2(e) (64 floats),
+  // D (64 floats). Wave 0 loads a tile's L into a register when the tile is
+  // requested and, once the loads have landed, stores -L log2(e) (-inf for a
+  // row that saw no key) into the stage just before the barrier that
+  // publishes it, so the per-row conversion is done once per tile, not by
+  // every lane that reads the row.
+  float l_next = 0.f;
   auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int qstart = t * BQ;
     const uint32_t valid = (uint32_t)(Nq - qstart) * RB;
@@ -367,8 +374,17 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
     }
     if (wave == 0) {
       const uint32_t svalid = (uint32_t)(Nq - qstart) * 4;
-      lds_dma4(make_rsrc_words(lh + qstart, svalid), (uint32_t)lane * 4, stage + 2 * TB);
+      // rows past the queries read L = 0 (their Q and dO rows are zero too)
+      l_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(lh + qstart, svalid), (uint32_t)lane * 4, 0, 0));
       lds_dma4(make_rsrc_words(deh + qstart, svalid), (uint32_t)lane * 4, stage + 2 * TB + C::K_STAT);
+    }
+  };
+  // called by every wave after wait_vmem() and before the barrier that
+  // publishes stage `buf`
+  auto publish_offsets = [&](int buf) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const float nl = (l_next == -INFINITY) ? -INFINITY : -l_next * 1.4426950408889634f;
+      *(FA_LDS float *)(smem + buf * C::K_BUF + 2 * TB + lane * 4) = nl;
     }
   };
   const TileOffsets<D> off(lane);
@@ -381,6 +397,7 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
   auto step = [&](int t, auto buf_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
     wait_vmem();
+    publish_offsets(buf);
     __syncthreads();
     if (t + 1 < n_qt) issue_tile(t + 1, buf ^ 1);
     const int qstart = t * BQ;
@@ -395,11 +412,20 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       // S = Q K^T and dP = dO V^T (queries x keys; a lane owns one key)
+      // every row fragment of the block is requested before the first MFMA
+      // (one wave per SIMD: nothing else hides the LDS latency)
       f32x16 s = f32x16{}, dp = f32x16{};
+      u32x4 qr[NKC], dr[NKC];
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        s = mfma16<DT>(lds_row_frag<D>(ql, off, kc, qb), kf[kc], s);
-        dp = mfma16<DT>(lds_row_frag<D>(dl, off, kc, qb), vf[kc], dp);
+        qr[kc] = lds_row_frag<D>(ql, off, kc, qb);
+        dr[kc] = lds_row_frag<D>(dl, off, kc, qb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mfma16<DT>(qr[kc], kf[kc], s);
+        dp = mfma16<DT>(dr[kc], vf[kc], dp);
       }
       // L and D of the 16 query rows this lane holds: rows 8*g + half*4 + 0..3
       float nl[16], dd[16];
@@ -410,9 +436,9 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
         const f32x4 dvv = *(const FA_LDS f32x4 *)(ds_ + r0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // rows past the queries read L = D = 0 and have zero Q and dO, so
-          // they contribute nothing; a row that saw no key (L = -inf) gets P = 0
-          nl[4 * g + j] = (lvv[j] == -INFINITY) ? -INFINITY : -lvv[j] * 1.4426950408889634f;
+          // rows past the queries have offset 0, D = 0 and zero Q and dO, so
+          // they contribute nothing; a row that saw no key has offset -inf: P = 0
+          nl[4 * g + j] = lvv[j];
           dd[4 * g + j] = dvv[j];
         }
       }
@@ -437,10 +463,16 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
           bs[w] = pack2<DT>(p0 * (dp[i] - dd[i]), p1 * (dp[i + 1] - dd[i + 1]));
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the 16 query rows of chunk pc
+        u32x4 ta[NDB], tb[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma16<DT>(lds_tr_frag<D>(dl, off, pc, db), bp, dv[db]);
-          dk[db] = mfma16<DT>(lds_tr_frag<D>(ql, off, pc, db), bs, dk[db]);
+          ta[db] = lds_tr_frag<D>(dl, off, pc, db);
+          tb[db] = lds_tr_frag<D>(ql, off, pc, db);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[db] = mfma16<DT>(ta[db], bp, dv[db]);
+          dk[db] = mfma16<DT>(tb[db], bs, dk[db]);
         }
       }
     }
