@@ -181,6 +181,36 @@ def test_cross_attention_long_keys_sampled():
     parity.check(o_s, l_s, o_ref, lse_ref, "bf16", "cross long keys")
 
 
+@pytest.mark.parametrize("causal,align", [(False, "top-left"), (True, "bottom-right")])
+def test_longest_key_sequence(causal, align):
+    """The largest key length one head may have at D = 128 bf16: the K and V
+    heads are 2^31 - 256 bytes, the limit of the kernels' 32-bit byte offsets
+    (one key more is rejected on the host). Three query rows over 8388607 keys
+    (the last tile ragged), single pass and split-KV, against the oracle; the
+    O check is also held to |O| of order 1 (a near-uniform average of 8M
+    values would be ~0 and pass any absolute tolerance)."""
+    D = 128
+    nk = (2 ** 31 - 1) // (D * 2)
+    nq = 3
+    _banner(f"longest key sequence Nk={nk} causal={causal} {align}")
+    qb, kb, vb = fa_inputs.draw_qkv_cross(1, 1, nq, nk, D, "bf16", 4343)
+    # Q x 8 (exact): the softmax concentrates on a few of the 8M keys, so O is
+    # of order 1 and its check is not trivially met
+    qb = fa_inputs.round_to_dtype(fa_inputs.to_f32(qb, "bf16") * 8.0, "bf16")
+    scale = parity.default_scale(D)
+    o1, l1 = _run_ex(qb, kb, vb, "bf16", causal, align, scale)
+    o2, l2 = _run_split(qb, kb, vb, "bf16", causal, align, scale, 0)
+    rows = np.array([[0, i] for i in range(nq)])
+    q, k, v = (fa_inputs.to_f32(x, "bf16") for x in (qb, kb, vb))
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, causal, rows, causal_align=align)
+    for what, o, l in (("single pass", o1, l1), ("split-KV", o2, l2)):
+        oe, le = parity.check(o.reshape(nq, D), l.reshape(nq), o_ref, lse_ref, "bf16",
+                              f"longest keys {what}")
+        print(f"[parity] longest keys {what} causal={causal}: O err {oe:.2e} LSE err {le:.2e}",
+              flush=True)
+    assert np.abs(o_ref).max() > 0.5
+
+
 # ---------------------------------------------------------------------------
 # Split-KV (fa_fwd_splitkv): the same attention, keys split over workgroups
 
