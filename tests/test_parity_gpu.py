@@ -526,3 +526,86 @@ def test_workload_full_size(name, causal):
           flush=True)
     # every output row is finite, and (non-degenerate inputs) LSE >= the row max
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# Streams and HIP graphs: the entry points are stream-ordered and make no
+# allocating or synchronising call, so they run on any stream and can be
+# captured into a graph
+
+
+def _graph_inputs(seed):
+    import torch
+    qb, kb, vb = fa_inputs.draw_qkv(2, 4, 520, 128, "bf16", seed)
+    dob = fa_inputs.draw_qkv(2, 4, 520, 128, "bf16", seed + 1)[0]
+    return tuple(parity.to_device(x, "bf16") for x in (qb, kb, vb, dob))
+
+
+def test_side_stream_matches_default_stream():
+    """Inputs written and attention run on a side stream give bitwise the
+    result of the default stream."""
+    import torch
+    _banner("side stream")
+    q, k, v, _ = _graph_inputs(501)
+    o_ref, l_ref = fa.fa_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q2, k2, v2 = q * 1, k * 1, v * 1          # produced on the side stream
+        o, lse = fa.fa_fwd(q2, k2, v2, causal=True, stream=side)
+    side.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_graph_capture_replays_match_eager():
+    """fa_fwd (both masks), fa_fwd_splitkv (two kernels, preallocated
+    workspace) and fa_bwd (two kernels) captured into one HIP graph; the
+    inputs are rewritten between replays by eager kernels, and every replay
+    must equal, bitwise, the eager calls on the same inputs."""
+    import torch
+    _banner("graph capture")
+    q, k, v, do = _graph_inputs(601)
+    o_nc, l_nc = torch.empty_like(q), torch.empty(q.shape[:3], device=q.device)
+    o_c, l_c = torch.empty_like(q), torch.empty(q.shape[:3], device=q.device)
+    o_s, l_s = torch.empty_like(q), torch.empty(q.shape[:3], device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], device=q.device)
+    B, H, N, D = q.shape
+    need = fa.fa_fwd_splitkv_workspace_size(B, H, N, N, D, 4)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+
+    def work(stream):
+        fa.fa_fwd(q, k, v, o_nc, l_nc, causal=False, stream=stream)
+        fa.fa_fwd(q, k, v, o_c, l_c, causal=True, stream=stream)
+        fa.fa_fwd_splitkv(q, k, v, o_s, l_s, causal=True, num_splits=4, workspace=ws,
+                          stream=stream)
+        fa.fa_bwd(q, k, v, o_c, do, l_c, causal=True, dq=dq, dk=dk, dv=dv, delta=delta,
+                  stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work(side)                                 # first calls outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs = (o_nc, l_nc, o_c, l_c, o_s, l_s, dq, dk, dv, delta)
+    for rep in range(4):
+        nq, nk, nv, ndo = _graph_inputs(700 + rep)
+        q.copy_(nq), k.copy_(nk), v.copy_(nv), do.copy_(ndo)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        work(torch.cuda.current_stream())           # eager, same inputs
+        torch.cuda.synchronize()
+        for name, g, e in zip(("o", "lse", "o_causal", "lse_causal", "o_split", "lse_split",
+                               "dq", "dk", "dv", "delta"), got, outs):
+            assert torch.equal(g, e), f"replay {rep}: {name} differs from the eager call"
+    # and the replayed forward is right, not only repeatable
+    bits = fa_inputs.draw_qkv(2, 4, 520, 128, "bf16", 703)
+    o_ref, lse_ref = oracle.attention(*(fa_inputs.to_f32(x, "bf16") for x in bits), D ** -0.5, True)
+    parity.check(parity.from_device(o_c), l_c.cpu().numpy(), o_ref, lse_ref, "bf16", "graph")
