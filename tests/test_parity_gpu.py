@@ -131,6 +131,33 @@ def test_cross_attention_full_parity(dtype, D, nq, nk, causal, align):
     parity.check(o, lse, o_ref, lse_ref, dtype, f"cross {dtype} D={D} {nq}x{nk} {causal} {align}")
 
 
+# The test matrix of "FlashAttention 2 from PyTorch to Triton" (Step 3): shapes
+# (batch, query rows, key rows, head dim) without a head axis (H = 1), fp32 and
+# bf16, causal only where the matrix is square. Its (1, 37, 53, 32) entry has a
+# head dimension outside {64, 128}, which the library rejects as unsupported.
+PAGE_MATRIX = [(4, 128, 128, 64), (2, 1024, 1024, 64), (2, 100, 100, 64), (1, 200, 96, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,nq,nk,D", PAGE_MATRIX)
+def test_pages_test_matrix(B, nq, nk, D, dtype):
+    _banner(f"pages' matrix B={B} Nq={nq} Nk={nk} D={D} {dtype}")
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, 1, nq, nk, D, dtype, 9000 + nq + nk + D)
+    scale = parity.default_scale(D)
+    for causal in ((False, True) if nq == nk else (False,)):
+        o, lse = _run_ex(qb, kb, vb, dtype, causal, "top-left", scale)
+        o_ref, lse_ref = parity.reference_full_ex(qb, kb, vb, dtype, scale, causal, "top-left")
+        parity.check(o, lse, o_ref, lse_ref, dtype, f"pages' matrix {B}x{nq}x{nk}x{D} causal={causal}")
+
+
+def test_pages_test_matrix_head_dim_32_is_rejected():
+    import torch
+    qb, kb, vb = fa_inputs.draw_qkv_cross(1, 1, 37, 53, 32, "bf16", 9001)
+    q, k, v = (parity.to_device(x, "bf16") for x in (qb, kb, vb))
+    with pytest.raises(fa.FAError):
+        fa.fa_fwd_ex(q, k, v, causal=False)
+
+
 def test_cross_attention_one_query_two_keys():
     """One query, two keys, equal scores, value rows 5 and 10: O = 7.5 and
     LSE = ln 2 exactly representable; top-left causal sees key 0 only (O = 5)."""
