@@ -29,10 +29,10 @@
 //
 // Causal attention stops the key loop after the tile's last query row and
 // applies the element mask only on tiles that straddle the diagonal or the
-// end of the keys. The diagonal is shifted by coff: 0 aligns it top-left,
-// nk - nq bottom-right ("How to profile and optimise kernels", Round 4,
-// on non-square causal attention) ("A09", section 3, Causal masking: skipping beats
-// masking; "How to profile and optimise kernels", Round 4).
+// end of the keys ("A09", section 3, Causal masking: skipping beats masking).
+// The diagonal is shifted by coff: 0 aligns it top-left, nk - nq bottom-right
+// ("How to profile and optimise kernels", Round 4, on non-square causal
+// attention).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -396,7 +396,8 @@ def test_bwd_unseen_keys_and_rows_are_zero():
 
 
 BWD_FULL_SIZE = [(fa_inputs.HEADLINE, False), (fa_inputs.HEADLINE, True),
-                 ("b2h16_n4000_d128_fp16", False), ("b2h16_n4000_d128_fp16", True)]
+                 ("b2h16_n4000_d128_fp16", False), ("b2h16_n4000_d128_fp16", True),
+                 ("b4h16_n4096_d64_bf16", False), ("b4h16_n4096_d64_bf16", True)]
 
 
 @pytest.mark.parametrize("name,causal", BWD_FULL_SIZE,
