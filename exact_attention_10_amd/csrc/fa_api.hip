@@ -44,11 +44,12 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// The default is the simple family; 16-bit non-causal D=128 runs it with 8
-// waves (256 query rows share each K/V tile), which measured fastest there,
-// and every other shape with 4.
+// The default is the simple family; 16-bit D=128 runs it with 8 waves (256
+// query rows share each K/V tile), which measured fastest there for both
+// masks (causal with paired query tiles), and every other shape with 4.
 int default_waves(int dtype, int64_t D, int causal) {
-  return (dtype != FA_DTYPE_FP32 && D == 128 && !causal) ? 8 : 4;
+  (void)causal;
+  return (dtype != FA_DTYPE_FP32 && D == 128) ? 8 : 4;
 }
 
 bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
@@ -113,6 +114,22 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse,
 
 void opt_in_lds(const void *fn, int bytes);
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  static std::mutex mu;
+  static int cache[64] = {0};
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 int launch(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t n_kv, int64_t D, int causal,
            int causal_align, float scale, int dtype, void *stream, int variant) {
@@ -123,7 +140,7 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   if (!pick(dtype, D, causal, kVariants[variant], &L)) return FA_ERR_UNSUPPORTED;
   if (L.lds > 65536) opt_in_lds(L.fn, L.lds);
 
-  fa::Params p;
+  fa::Params p = {};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -139,7 +156,12 @@ int launch(const void *q, const void *k, const void *v, void *o, float *lse,
   // scale * log2(e), formed in double and rounded once
   p.c = (float)((double)scale * 1.4426950408889634);
 
-  const dim3 grid((unsigned)(B * H * p.nq_tiles));
+  // causal kernels that can pair query tiles take one workgroup per (head,
+  // pair of tiles) when that grid still gives every CU a workgroup
+  const int64_t pairs = (p.nq_tiles + 1) / 2;
+  p.pair = (causal && L.paired && B * H * pairs >= cu_count()) ? 1 : 0;
+  const int64_t per_head = p.pair ? pairs : p.nq_tiles;
+  const dim3 grid((unsigned)(B * H * per_head));
   const dim3 block((unsigned)L.threads);
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(L.fn, grid, block, args, (size_t)L.lds,
@@ -210,7 +232,7 @@ int launch_splitkv(const void *q, const void *k, const void *v, void *o, float *
   if (!L.fn || !comb) return FA_ERR_UNSUPPORTED;
   if (L.lds > 65536) opt_in_lds(L.fn, L.lds);
 
-  fa::Params p;
+  fa::Params p = {};
   p.q = q;
   p.k = k;
   p.v = v;

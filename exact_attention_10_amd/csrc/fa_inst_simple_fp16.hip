@@ -8,7 +8,7 @@ namespace {
 template <int D, bool CAUSAL, int W>
 FaLaunch make() {
   using C = fa::Cfg<fa::DT_FP16, D, CAUSAL, W>;
-  return {reinterpret_cast<const void *>(&fa::fa_fwd_kernel<fa::DT_FP16, D, CAUSAL, W>), C::LDS_BYTES, C::BM, W * 64};
+  return {reinterpret_cast<const void *>(&fa::fa_fwd_kernel<fa::DT_FP16, D, CAUSAL, W>), C::LDS_BYTES, C::BM, W * 64, CAUSAL ? 1 : 0};
 }
 template <int W>
 FaLaunch by_d(int d, bool causal) {

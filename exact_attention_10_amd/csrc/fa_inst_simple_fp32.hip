@@ -7,7 +7,7 @@ namespace {
 template <int D, bool CAUSAL>
 FaLaunch make() {
   using C = fa::Cfg<fa::DT_FP32, D, CAUSAL>;
-  return {reinterpret_cast<const void *>(&fa::fa_fwd_kernel<fa::DT_FP32, D, CAUSAL>), C::LDS_BYTES, C::BM, 256};
+  return {reinterpret_cast<const void *>(&fa::fa_fwd_kernel<fa::DT_FP32, D, CAUSAL>), C::LDS_BYTES, C::BM, 256, CAUSAL ? 1 : 0};
 }
 }  // namespace
 

@@ -79,6 +79,8 @@ struct Params {
   int n_heads;         // B*H
   float *o_part;       // [n_splits][BH][nq][D]
   float *lse_part;     // [n_splits][BH][nq]
+  // causal single pass: 1 = one workgroup per (head, pair of query tiles)
+  int pair;
 };
 
 constexpr int kMaxSplits = 32;
@@ -217,8 +219,32 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     split = rest % p.n_splits;
     rest /= p.n_splits;
   }
-  const int bh = rest;
+  int bh = rest;
   if (CAUSAL) qt = p.nq_tiles - 1 - qt;    // longest causal tiles first
+  // Causal, single pass, with p.pair: the grid has one workgroup per (head,
+  // pair of query tiles) and each workgroup runs the long tile T-1-i, then
+  // the short tile i, so every workgroup does the same T+1 tile-rows of work
+  // (the middle tile of an odd T runs alone). Equal work per workgroup removes
+  // the tail of unequal ones and spreads the short tiles' fixed costs; the
+  // host pairs only grids that still fill the chip.
+  int second_qt = -1;
+  if (CAUSAL && !SPLIT && p.pair) {
+    const int T = p.nq_tiles;
+    const int npairs = (T + 1) / 2;
+    const int nvalid = (int)gridDim.x;     // heads x pairs
+    int c = blockIdx.x;
+    if (p.xcd_remap && (nvalid & 7) == 0) c = (c & 7) * (nvalid >> 3) + (c >> 3);
+    bh = c / npairs;
+    const int pr = c - bh * npairs;
+    qt = T - 1 - pr;
+    second_qt = (pr != T - 1 - pr) ? pr : -1;
+  }
+  for (int job = 0; job < 2; ++job) {
+  if (job == 1) {
+    if (second_qt < 0) break;
+    qt = second_qt;
+    __syncthreads();                       // every wave is done with the first tile's LDS
+  }
   // Query and key lengths are separate ("Triton: FlashAttention-2 Forward
   // Pass", Masks and sentinels): Q rows, the output and LSE use nq; the key
   // loop and the K/V rows use nk (and the key-length mask n_kv).
@@ -554,6 +580,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
       p.lse[(int64_t)bh * Nq + my_q] = lse;
     }
   }
+  }   // job
 }
 
 }  // namespace fa

@@ -10,6 +10,7 @@ struct FaLaunch {
   int lds;          // dynamic LDS bytes per workgroup
   int bm;           // query rows per workgroup
   int threads;      // threads per workgroup
+  int paired = 0;   // causal grid of (head, pair of query tiles): one workgroup per pair
 };
 
 // dt: 0 fp32, 1 fp16, 2 bf16 (the values of the fa.h dtype codes); d: 64 or 128
