@@ -310,7 +310,7 @@ int launch_bwd(const void *q, const void *k, const void *v, const void *o, const
   if (L.dq_lds > 65536) opt_in_lds(L.dq_fn, L.dq_lds);
   if (L.dkdv_lds > 65536) opt_in_lds(L.dkdv_fn, L.dkdv_lds);
 
-  fa::BwdParams p;
+  fa::BwdParams p = {};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -330,14 +330,16 @@ int launch_bwd(const void *q, const void *k, const void *v, const void *o, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   p.n_tiles = (int)((Nq + 127) / 128);
+  p.pair = (causal && B * H * ((p.n_tiles + 1) / 2) >= cu_count()) ? 1 : 0;
   void *args[] = {&p};
-  hipError_t e = hipLaunchKernel(L.dq_fn, dim3((unsigned)(B * H * p.n_tiles)), dim3(256), args,
+  hipError_t e = hipLaunchKernel(L.dq_fn, dim3((unsigned)(B * H * (p.pair ? (p.n_tiles + 1) / 2 : p.n_tiles))), dim3(256), args,
                                  (size_t)L.dq_lds, st);
   if (e == hipSuccess) {
     fa::BwdParams p2 = p;
     p2.n_tiles = (int)nk_tiles;
+    p2.pair = (causal && B * H * ((p2.n_tiles + 1) / 2) >= cu_count()) ? 1 : 0;
     void *args2[] = {&p2};
-    e = hipLaunchKernel(L.dkdv_fn, dim3((unsigned)(B * H * p2.n_tiles)), dim3(256), args2,
+    e = hipLaunchKernel(L.dkdv_fn, dim3((unsigned)(B * H * (p2.pair ? (p2.n_tiles + 1) / 2 : p2.n_tiles))), dim3(256), args2,
                         (size_t)L.dkdv_lds, st);
   }
   if (e != hipSuccess) {

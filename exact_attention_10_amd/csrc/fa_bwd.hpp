@@ -38,8 +38,9 @@ struct BwdParams {
   void *dq, *dk, *dv;                 // like q, k, v
   int64_t nq, nk;
   int64_t coff;                       // causal: query i sees keys j <= i + coff
-  int n_tiles;                        // workgroups per head: query tiles (dq) or key tiles (dkdv)
+  int n_tiles;                        // query tiles (dq) or key tiles (dkdv) per head
   int xcd_remap;
+  int pair;                           // causal: one workgroup per (head, pair of tiles)
   float c;                            // scale * log2(e)
   float scale;
 };
@@ -168,6 +169,33 @@ __device__ __forceinline__ int remap_block(int bid, int nblk, int xcd_remap) {
   return (xcd_remap && (nblk & 7) == 0) ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
 }
 
+// The (head, tile) jobs of a workgroup. Causal work per tile grows (dQ: with
+// the query tile) or shrinks (dK/dV: with the key tile) linearly, so with
+// p.pair a workgroup takes tiles i and n_tiles-1-i, the longer first, and
+// every workgroup does the same work; otherwise one tile per workgroup.
+struct BwdJobs {
+  int bh, first, second;   // second < 0: a single job
+};
+__device__ __forceinline__ BwdJobs bwd_jobs(const BwdParams &p, bool causal, bool work_grows) {
+  const int T = p.n_tiles;
+  const int c = remap_block(blockIdx.x, gridDim.x, p.xcd_remap);
+  BwdJobs j;
+  if (causal && p.pair) {
+    const int npairs = (T + 1) / 2;
+    j.bh = c / npairs;
+    const int pr = c - j.bh * npairs;
+    const int lo = pr, hi = T - 1 - pr;
+    j.first = work_grows ? hi : lo;
+    j.second = (lo != hi) ? (work_grows ? lo : hi) : -1;
+  } else {
+    j.bh = c / T;
+    j.first = c - j.bh * T;
+    if (causal && work_grows) j.first = T - 1 - j.first;   // longest first
+    j.second = -1;
+  }
+  return j;
+}
+
 // ---------------------------------------------------------------------------
 // dQ (and D) kernel
 
@@ -179,10 +207,14 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dq_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int bid = remap_block(blockIdx.x, gridDim.x, p.xcd_remap);
-  const int bh = bid / p.n_tiles;
-  int qt = bid - bh * p.n_tiles;
-  if (CAUSAL) qt = p.n_tiles - 1 - qt;
+  const BwdJobs jobs = bwd_jobs(p, CAUSAL, true);
+  const int bh = jobs.bh;
+  for (int job = 0; job < 2; ++job) {
+  if (job == 1) {
+    if (jobs.second < 0) break;
+    __syncthreads();                     // every wave is done with the first tile's LDS
+  }
+  const int qt = job == 0 ? jobs.first : jobs.second;
   const int64_t Nq = p.nq;
   const int Nk = (int)p.nk, coff = (int)p.coff;
   const int q0 = qt * BM, qw = q0 + wave * 32, my_q = qw + l32;
@@ -303,6 +335,7 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dq_kernel(BwdParams p) {
     if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
   }
   if (row_ok) store_rows<DT, D>(p.dq, (int64_t)bh * Nq + my_q, acc, p.scale, half);
+  }   // job
 }
 
 // ---------------------------------------------------------------------------
@@ -317,9 +350,14 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int bid = remap_block(blockIdx.x, gridDim.x, p.xcd_remap);
-  const int bh = bid / p.n_tiles;
-  const int kt = bid - bh * p.n_tiles;
+  const BwdJobs jobs = bwd_jobs(p, CAUSAL, false);
+  const int bh = jobs.bh;
+  for (int job = 0; job < 2; ++job) {
+  if (job == 1) {
+    if (jobs.second < 0) break;
+    __syncthreads();                     // every wave is done with the first tile's LDS
+  }
+  const int kt = job == 0 ? jobs.first : jobs.second;
   const int Nq = (int)p.nq, Nk = (int)p.nk, coff = (int)p.coff;
   const int k0 = kt * BKEYS, kw = k0 + wave * 32, my_key = kw + l32;
   const bool key_ok = my_key < Nk;
@@ -487,6 +525,7 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
     store_rows<DT, D>(p.dk, (int64_t)bh * Nk + my_key, dk, p.scale, half);
     store_rows<DT, D>(p.dv, (int64_t)bh * Nk + my_key, dv, 1.0f, half);
   }
+  }   // job
 }
 
 }  // namespace fa
