@@ -247,6 +247,36 @@ def test_longest_key_sequence(causal, align):
     assert np.abs(o_ref).max() > 0.5
 
 
+@pytest.mark.parametrize("align", ["top-left", "bottom-right"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_paired_causal_cross_sampled(D, align):
+    """Causal grids large enough for paired query / key tiles (128 heads),
+    with Nq != Nk and both alignments: the forward on sampled rows and the
+    backward (dQ rows, dK/dV key rows) of two heads against the oracle."""
+    B, H, nq, nk = 8, 16, 1000, 2500
+    _banner(f"paired causal cross D={D} {align}")
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, "bf16", 5150 + D)
+    dob = fa_inputs.draw_qkv_cross(B, H, nq, 1, D, "bf16", 5151 + D)[0]
+    scale = parity.default_scale(D)
+    dq, dk, dv, _, o = _run_fwd_bwd(qb, kb, vb, dob, "bf16", True, align, scale)
+    o = o.reshape(B * H, nq, D)
+    rows = parity.sample_rows(B, H, nq, 160, seed=D)
+    q, k, v, do = (fa_inputs.to_f32(x, "bf16") for x in (qb, kb, vb, dob))
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, True, rows, causal_align=align)
+    parity.check(o[rows[:, 0], rows[:, 1]], None, o_ref, lse_ref, "bf16", f"paired fwd {align}")
+    rng = np.random.default_rng(D)
+    edge = np.array([0, 1, 127, 128, nq - 1])
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        r = np.unique(np.concatenate([edge, rng.integers(0, nq, 16)]))
+        c = np.unique(np.concatenate([[0, 127, 128, nk - nq - 1, nk - nq, nk - 1],
+                                      rng.integers(0, nk, 16)]))
+        dq_r, dk_r, dv_r = oracle.attention_bwd_sampled(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                        scale, True, r, c, causal_align=align)
+        for n, g, ref in (("dQ", dq[b, h, r], dq_r), ("dK", dk[b, h, c], dk_r),
+                          ("dV", dv[b, h, c], dv_r)):
+            parity.check_grad(g, ref, "bf16", f"paired bwd {align} head ({b},{h}) {n}")
+
+
 # ---------------------------------------------------------------------------
 # Split-KV (fa_fwd_splitkv): the same attention, keys split over workgroups
 
