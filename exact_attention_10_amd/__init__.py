@@ -223,6 +223,8 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, *, causal=False, causal_align="top
     need = lib.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, int(num_splits))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
@@ -263,6 +265,9 @@ def fa_bwd(q, k, v, o, dout, lse, *, causal=False, causal_align="top-left", scal
             raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
     if delta is None:
         delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif delta.shape != (B, H, Nq) or delta.dtype != torch.float32 or not delta.is_contiguous() \
+            or delta.device != q.device:
+        raise ValueError("delta must be a contiguous fp32 [B, H, Nq] tensor on q's device")
     rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                     B, H, Nq, Nk, D, int(bool(causal)), _ALIGN[causal_align], float(scale),

@@ -391,6 +391,24 @@ def _run_fwd_bwd(qb, kb, vb, dob, dtype, causal, align, scale):
             delta.cpu().numpy(), parity.from_device(o))
 
 
+def test_binding_rejects_mismatched_delta_and_workspace():
+    """Caller-provided buffers the kernels write are checked before any launch:
+    a too-short or wrongly typed delta for fa_bwd, a workspace on the host for
+    fa_fwd_splitkv."""
+    import torch
+    _banner("binding checks of delta and workspace")
+    qb, kb, vb = fa_inputs.draw_qkv(1, 2, 64, 64, "bf16", 77)
+    q, k, v = (parity.to_device(x, "bf16") for x in (qb, kb, vb))
+    o, lse = fa.fa_fwd(q, k, v)
+    for bad in (torch.empty((1, 2, 32), dtype=torch.float32, device=q.device),
+                torch.empty((1, 2, 64), dtype=torch.float16, device=q.device)):
+        with pytest.raises(ValueError):
+            fa.fa_bwd(q, k, v, o, o, lse, delta=bad)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_splitkv(q, k, v, num_splits=2, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()
+
+
 BWD_SHAPES = [(64, 64), (130, 130), (37, 200), (200, 37), (1, 65), (128, 300), (257, 511)]
 
 
