@@ -247,6 +247,25 @@ def test_longest_key_sequence(causal, align):
     assert np.abs(o_ref).max() > 0.5
 
 
+@pytest.mark.parametrize("dtype,D", [("fp32", 64), ("fp16", 64), ("fp16", 128)])
+def test_paired_causal_dtypes_sampled(dtype, D):
+    """Causal grids of 32 heads at N = 4096 pair query tiles for every dtype
+    (the fp32 and fp16 instances share the pairing with bf16); sampled rows,
+    including both ends of every paired tile, against the oracle."""
+    B, H, N = 4, 8, 4096
+    _banner(f"paired causal dtype={dtype} D={D}")
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 5300 + D + (1 if dtype == "fp16" else 0))
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, dtype, True, scale)
+    o = o.reshape(B * H, N, D)
+    lse = lse.reshape(B * H, N)
+    bm = 128 if (dtype == "fp32" or D == 64) else 256
+    rows = parity.sample_rows(B, H, N, 200, seed=D + 3, bm=bm)
+    o_ref, lse_ref = parity.reference_rows(qb, kb, vb, dtype, scale, True, rows)
+    parity.check(o[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], o_ref, lse_ref, dtype,
+                 f"paired causal {dtype} D={D}")
+
+
 @pytest.mark.parametrize("align", ["top-left", "bottom-right"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_paired_causal_cross_sampled(D, align):
