@@ -382,7 +382,8 @@ def main():
     extra = {}
     if not a.no_extra:
         for name, causal in ((w.name, True), ("b4h16_n4096_d64_bf16", False),
-                             ("b4h16_n4096_d64_bf16", True), ("b1h32_n16384_d128_bf16_q8", True)):
+                             ("b4h16_n4096_d64_bf16", True), ("b2h16_n4000_d128_fp16", False),
+                             ("b2h16_n4000_d128_fp16", True), ("b1h32_n16384_d128_bf16_q8", True)):
             r = time_gpu(fa_inputs.WORKLOADS[name], causal, max(10, a.steps // 2),
                          max(5, a.warmup // 2), torch, fa)
             key = f"{name}_{'causal' if causal else 'noncausal'}"
