@@ -266,6 +266,35 @@ def test_paired_causal_dtypes_sampled(dtype, D):
                  f"paired causal {dtype} D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_paired_causal_odd_tiles_sampled(D):
+    """129 heads of 600 rows: an odd number of query tiles (and of the
+    backward's key tiles), so one workgroup per head runs the middle tile
+    alone, on a paired grid whose size is not a multiple of 8 (no XCD
+    reordering). Forward on sampled rows, dQ, dK, dV of three heads."""
+    B, H, N = 1, 129, 600
+    _banner(f"paired causal odd tiles D={D}")
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, "bf16", 5400 + D)
+    dob = fa_inputs.draw_qkv(B, H, N, D, "bf16", 5401 + D)[0]
+    scale = parity.default_scale(D)
+    dq, dk, dv, _, o = _run_fwd_bwd(qb, kb, vb, dob, "bf16", True, "top-left", scale)
+    o = o.reshape(B * H, N, D)
+    bm = 128 if D == 64 else 256
+    rows = parity.sample_rows(B, H, N, 160, seed=D + 11, bm=bm)
+    q, k, v, do = (fa_inputs.to_f32(x, "bf16") for x in (qb, kb, vb, dob))
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, True, rows)
+    parity.check(o[rows[:, 0], rows[:, 1]], None, o_ref, lse_ref, "bf16", f"odd tiles fwd D={D}")
+    rng = np.random.default_rng(D)
+    edge = np.array([0, 127, 128, 255, 256, 383, 384, 511, 512, N - 1])
+    for h in (0, H // 2, H - 1):
+        r = np.unique(np.concatenate([edge, rng.integers(0, N, 12)]))
+        dq_r, dk_r, dv_r = oracle.attention_bwd_sampled(q[0, h], k[0, h], v[0, h], do[0, h],
+                                                        scale, True, r, r)
+        for n, g, ref in (("dQ", dq[0, h, r], dq_r), ("dK", dk[0, h, r], dk_r),
+                          ("dV", dv[0, h, r], dv_r)):
+            parity.check_grad(g, ref, "bf16", f"odd tiles bwd D={D} head {h} {n}")
+
+
 @pytest.mark.parametrize("align", ["top-left", "bottom-right"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_paired_causal_cross_sampled(D, align):
