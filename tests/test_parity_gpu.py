@@ -295,6 +295,23 @@ def test_paired_causal_odd_tiles_sampled(D):
             parity.check_grad(g, ref, "bf16", f"odd tiles bwd D={D} head {h} {n}")
 
 
+@pytest.mark.parametrize("n_kv", [0, 1, 300, 599])
+def test_paired_causal_key_length_mask_sampled(n_kv):
+    """The key-length mask on a paired causal grid (129 heads x 3 tiles of
+    256 rows): sampled rows against the oracle with the same n_kv."""
+    B, H, N, D = 1, 129, 600, 128
+    _banner(f"paired causal n_kv={n_kv}")
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, "bf16", 5500 + n_kv)
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, "bf16", True, scale, n_kv=n_kv)
+    o = o.reshape(B * H, N, D)
+    lse = lse.reshape(B * H, N)
+    rows = parity.sample_rows(B, H, N, 160, seed=n_kv, bm=256)
+    o_ref, lse_ref = parity.reference_rows(qb, kb, vb, "bf16", scale, True, rows, n_kv=n_kv)
+    parity.check(o[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16",
+                 f"paired causal n_kv={n_kv}")
+
+
 @pytest.mark.parametrize("align", ["top-left", "bottom-right"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_paired_causal_cross_sampled(D, align):
