@@ -345,7 +345,7 @@ template <int DT, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   constexpr int RB = C::RB, NKC = C::NKC, NDB = C::NDB, BQ = C::K_BQ, TB = C::K_TILE;
-  constexpr int BKEYS = 128, NQB = BQ / 32, NPC = BQ / 16;
+  constexpr int BKEYS = 128, NQB = BQ / 32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;

@@ -275,7 +275,6 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   // ---- Q fragments (B operand of S^T = K Q^T), straight from global ----
   // lane (q = l32, half) holds Q[my_q][kc*KSTEP + half*KSTEP/2 ...]
   constexpr int QE = KSTEP / 2;             // elements per lane per fragment
-  typedef uint16_t qraw_t __attribute__((ext_vector_type(8)));
   const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qh, (uint32_t)(q_head * ES));
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
