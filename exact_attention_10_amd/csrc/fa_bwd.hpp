@@ -50,8 +50,10 @@ __device__ __forceinline__ void lds_dma4(i32x4 rsrc, uint32_t voffset, uint32_t 
   i32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(r)
+  // the LDS base goes to m0 through an operand constraint, so the compiler
+  // knows that m0 is written here
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(r), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 

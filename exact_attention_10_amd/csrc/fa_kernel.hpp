@@ -118,8 +118,10 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t
   i32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(r)
+  // the LDS base goes to m0 through an operand constraint, so the compiler
+  // knows that m0 is written here
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(r), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 
@@ -403,13 +405,24 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, __uint_as_float(qf[kc][0]), s[kb], 0, 0, 0);
         }
     } else {
+      // The K fragments stream through a window of KPIPE head-dim chunks:
+      // chunk kc + KPIPE is requested before chunk kc's MFMAs are issued, so
+      // each MFMA finds its operand already in registers. Scheduling fences
+      // keep this order; left alone, the compiler sinks every read next to
+      // its MFMA, and each pair of MFMAs then waits a full LDS round trip
+      // unless the other wave of the SIMD has work to fill it.
+      constexpr int KPIPE = NKC < 4 ? NKC : 4;
       u32x4 kf[NKC][NKB];
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
+      auto read_k = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) kf[kc][kb] = *(const FA_LDS u32x4 *)(kl + k_off[kc] + kb * 32 * RB);
+      };
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
+      for (int kc = 0; kc < KPIPE; ++kc) read_k(kc);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        if (kc + KPIPE < NKC) read_k(kc + KPIPE);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const u32x4 b = {qf[kc][0], qf[kc][1], qf[kc][2], qf[kc][3]};
@@ -418,6 +431,8 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
           else
             s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[kc][kb]), __builtin_bit_cast(f16x8, b), s[kb], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // V^T fragments for this tile's PV, read now so that they arrive while
