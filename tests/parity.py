@@ -98,6 +98,47 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     return o_err, lse_err
 
 
+def check_every_row(o_gpu, lse_gpu, q_bits, k_bits, v_bits, dtype, scale, causal, what="",
+                    chunk=16384):
+    """Compare every output element and every LSE of a [B, H, N, D] result
+    with the fp64 oracle, which is evaluated in chunks of query rows so that
+    memory stays bounded at any size. The tolerances are those of check().
+    Returns (o_err, lse_err, worst): o_err in the metric of the dtype, and
+    worst = (head, row, d, |O_ref| there) for the largest O difference."""
+    B, H, N, D = q_bits.shape
+    BH = B * H
+    q, k, v = (fa_inputs.to_f32(x, dtype).reshape(BH, N, D) for x in (q_bits, k_bits, v_bits))
+    o_gpu = np.asarray(o_gpu).reshape(BH * N, D)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64).reshape(BH * N)
+    assert np.isfinite(o_gpu).all(), f"{what}: non-finite O"
+    diff_max, ref_max, lse_err, worst = 0.0, 0.0, 0.0, None
+    for start in range(0, BH * N, chunk):
+        idx = np.arange(start, min(start + chunk, BH * N), dtype=np.int64)
+        rows = np.stack([idx // N, idx % N], axis=1)
+        o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, causal, rows)
+        d = np.abs(o_gpu[idx].astype(np.float64) - o_ref)
+        at = np.unravel_index(np.argmax(d), d.shape)
+        if d[at] > diff_max:
+            diff_max = float(d[at])
+            r = int(idx[at[0]])
+            worst = (r // N, r % N, int(at[1]), float(abs(o_ref[at])))
+        ref_max = max(ref_max, float(np.abs(o_ref).max()))
+        lg = lse_gpu[idx]
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(fin, np.isfinite(lg)), f"{what}: LSE finiteness differs"
+        assert (lg[~fin] == lse_ref[~fin]).all(), f"{what}: LSE infinities differ"
+        if fin.any():
+            lse_err = max(lse_err, float(np.abs(lg[fin] - lse_ref[fin]).max()))
+    if dtype == "fp32":
+        o_err = diff_max / ref_max if ref_max > 0 else diff_max
+        assert o_err <= TOL_O_32_NORMWISE, f"{what}: fp32 O normwise error {o_err:.3e}"
+    else:
+        o_err = diff_max
+        assert o_err <= TOL_O_16, f"{what}: O max abs error {o_err:.3e} at {worst}"
+    assert lse_err <= TOL_LSE, f"{what}: LSE max abs error {lse_err:.3e}"
+    return o_err, lse_err, worst
+
+
 def reference_full(q_bits, k_bits, v_bits, dtype, scale, causal, n_kv=None):
     q, k, v = (fa_inputs.to_f32(x, dtype) for x in (q_bits, k_bits, v_bits))
     return oracle.attention(q, k, v, scale, causal, n_kv=n_kv)
