@@ -26,7 +26,9 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(_HERE, "libfa_mi355x.so")
+# the in-tree build; FA_MI355X_LIBRARY names another build of the same
+# sources instead (the tests use it for a host-sanitizer check build)
+LIBRARY = os.environ.get("FA_MI355X_LIBRARY") or os.path.join(_HERE, "libfa_mi355x.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_CAUSAL_TOP_LEFT, FA_CAUSAL_BOTTOM_RIGHT = 0, 1

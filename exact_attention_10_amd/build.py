@@ -57,14 +57,29 @@ def _run(cmd, cwd=None):
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for a CPU-only
+# check build of the library: each option reaches the host compilation only
+# (device code is never instrumented). The resulting library needs the clang
+# ASan runtime preloaded into the process that loads it.
+HOST_SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
 def build(output: str = LIBRARY, save_temps: str | None = None, verbose: bool = False,
-          jobs: int | None = None) -> str:
+          jobs: int | None = None, host_sanitize: bool = False) -> str:
     """Compile every translation unit in parallel and link the shared library.
     The library is written to a temporary name and renamed into place, so a
-    failed build never leaves a partial file behind."""
+    failed build never leaves a partial file behind. host_sanitize builds the
+    host code with ASan and UBSan (a check build, never the product)."""
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
     objdir = tempfile.mkdtemp(prefix="fa_build_")
     base = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    if host_sanitize:
+        base += HOST_SANITIZE_FLAGS
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
         base.insert(1, "-save-temps")
@@ -80,7 +95,10 @@ def build(output: str = LIBRARY, save_temps: str | None = None, verbose: bool = 
         for f in [ex.submit(_run, c, save_temps) for c in cmds]:
             f.result()
     tmp = output + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if host_sanitize:
+        link[1:1] = HOST_SANITIZE_FLAGS
+    _run(link)
     os.replace(tmp, output)
     for o in objs:
         os.unlink(o)
