@@ -7,14 +7,19 @@ one JSON line: attention TFLOP/s (4*B*H*N^2*D FLOPs, halved for causal, the
 count of "FlashAttention 2 from PyTorch to Triton", Step 4), the fraction of
 the MI355X dense bf16 MFMA peak, the same figures for the causal mask and the
 other N=4096 workload in "extra", and the fp64 CPU oracle timed on a bounded
-sample of the same workload as "cpu_baseline". "extra" also holds per-launch
+sample of the same workload as "cpu_baseline" (with every other benchmarked
+workload and mask sampled the same way). "extra" also holds per-launch
 percentiles (back to back, and with the caches scrubbed before each call),
 the split-KV and backward timings; "clock" holds the graphics clock and
 socket power read while the headline call runs back to back, and the
 roofline adds the fraction of the peak scaled to that clock.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                       [--no-clock]
+Every timed line follows `--warmup` calls and at least `--settle` seconds
+(default 1) of untimed back-to-back calls, so that the board has reached the
+clock it holds under sustained load; "timing" records the settle.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--no-cpu-baseline]
+                       [--no-extra] [--no-clock] [--counters-run REPS]
 """
 from __future__ import annotations
 
@@ -94,8 +99,18 @@ def stored_traffic():
         return None
 
 
+_BITS = {}
+
+
+def workload_bits(w):
+    """The workload's seeded input bits, drawn once per process."""
+    if w.name not in _BITS:
+        _BITS[w.name] = fa_inputs.workload_inputs(w)
+    return _BITS[w.name]
+
+
 def _device_inputs(w, torch):
-    qb, kb, vb = fa_inputs.workload_inputs(w)
+    qb, kb, vb = workload_bits(w)
     dt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
 
     def dev(b):
@@ -106,11 +121,39 @@ def _device_inputs(w, torch):
     return (dev(qb), dev(kb), dev(vb)), (qb, kb, vb)
 
 
-def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False):
-    """Whole-run timing: `warmup` untimed calls, then `steps` calls bracketed
-    by synchronisation and events on the launch stream (fa_fwd, kernel
-    variant `variant` through fa_fwd_variant, or fa_fwd_splitkv with the
-    library's split choice and a workspace allocated before timing)."""
+def settle(call, stream, torch, seconds, probes=10):
+    """Run `call` back to back for at least `seconds` of wall time, so that the
+    board reaches the clock and power state it holds under sustained load
+    ("How to profile and optimise kernels", How I profile: warm up for about a
+    second before timing). Returns the time spent, the number of calls and
+    the per-launch durations (ms) of `probes` calls made at the end."""
+    t0 = time.perf_counter()
+    n, batch = 0, 4
+    while True:
+        for _ in range(batch):
+            call()
+        torch.cuda.synchronize()
+        n += batch
+        elapsed = time.perf_counter() - t0
+        if elapsed >= seconds:
+            break
+        batch = min(batch * 2, 512)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(probes)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return elapsed, n, [round(e0.elapsed_time(e1), 5) for e0, e1 in ev]
+
+
+def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False, settle_s=1.0):
+    """Whole-run timing: `warmup` untimed calls, then at least `settle_s`
+    seconds of untimed back-to-back calls, then `steps` calls bracketed by
+    synchronisation and events on the launch stream (fa_fwd, kernel variant
+    `variant` through fa_fwd_variant, or fa_fwd_splitkv with the library's
+    split choice and a workspace allocated before timing)."""
     (q, k, v), _ = _device_inputs(w, torch)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
@@ -132,6 +175,7 @@ def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    settled_s, settle_calls, settle_last = settle(call, stream, torch, settle_s)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
@@ -143,7 +187,8 @@ def time_gpu(w, causal, steps, warmup, torch, fa, variant=None, splitkv=False):
     ms = start.elapsed_time(end) / steps
     flops = attention_flops(w.B, w.H, w.N, w.D, causal)
     return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,
-            "flops": flops}
+            "flops": flops, "settle_s": round(settled_s, 3), "settle_calls": settle_calls,
+            "settle_last_ms": settle_last}
 
 
 class ClockSampler:
@@ -234,19 +279,20 @@ def measure_clock(w, torch, fa, seconds=3.0, settle_s=1.2):
                       f"{seconds:.0f} s, readings after the first {settle_s:.1f} s"}
 
 
-def time_per_launch(w, causal, reps, torch, fa, scrub_mib=0):
+def time_per_launch(w, causal, reps, torch, fa, scrub_mib=0, settle_s=1.0):
     """Per-launch durations (median, p10, p90 in ms) from one event pair
     around each fa_fwd call; with scrub_mib > 0 each call is preceded by an
     untimed write of that many MiB, so that K and V start outside the L2 and
-    the memory-side cache."""
+    the memory-side cache. The calls follow `settle_s` seconds of back-to-back
+    calls."""
     (q, k, v), _ = _device_inputs(w, torch)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
     scrub = (torch.empty(scrub_mib << 18, dtype=torch.float32, device=q.device)
              if scrub_mib else None)
-    for _ in range(10):
-        fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
+    settle(lambda: fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream),
+           stream, torch, settle_s)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
     for e0, e1 in events:
@@ -263,9 +309,10 @@ def time_per_launch(w, causal, reps, torch, fa, scrub_mib=0):
             "scrub_mib": scrub_mib}
 
 
-def time_bwd(w, causal, steps, warmup, torch, fa):
+def time_bwd(w, causal, steps, warmup, torch, fa, settle_s=1.0):
     """Backward timing: the forward runs once untimed for O and LSE, then
-    `warmup` + `steps` fa_bwd calls, timed like time_gpu."""
+    `warmup` calls, `settle_s` seconds of calls and `steps` timed fa_bwd
+    calls, timed like time_gpu."""
     (q, k, v), _ = _device_inputs(w, torch)
     g = torch.Generator(device=q.device)
     g.manual_seed(w.seed + 1000)
@@ -281,6 +328,7 @@ def time_bwd(w, causal, steps, warmup, torch, fa):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    settle(call, stream, torch, settle_s)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(steps):
@@ -292,31 +340,113 @@ def time_bwd(w, causal, steps, warmup, torch, fa):
     return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def cpu_baseline(w, causal, target_s=15.0):
-    """The fp64 oracle on a bounded sample of rows of the same workload."""
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_one(w, causal, target_s, rng):
+    """The fp64 oracle (as it stands) on a bounded random sample of query rows
+    of one workload and mask: a probe of 256 rows sizes the sample to about
+    `target_s` seconds. Returns oracle TFLOP/s with the benchmark's FLOP count
+    per row (4*D per visible key), rows, seconds."""
     import oracle
-    threads = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    qb, kb, vb = fa_inputs.workload_inputs(w)
+    qb, kb, vb = workload_bits(w)
     q, k, v = (fa_inputs.to_f32(x, w.dtype) for x in (qb, kb, vb))
-    rng = np.random.default_rng(123)
     BH = w.B * w.H
 
     def run(n_rows):
         rows = np.stack([rng.integers(0, BH, n_rows), rng.integers(0, w.N, n_rows)], 1)
-        flops = sum(4 * ((i + 1) if causal else w.N) * w.D for i in rows[:, 1])
+        flops = float(sum(4 * ((int(i) + 1) if causal else w.N) * w.D for i in rows[:, 1]))
         t0 = time.perf_counter()
         oracle.attention_rows(q, k, v, w.scale, causal, rows)
         return time.perf_counter() - t0, flops
 
-    probe_rows = 2048
-    t, f = run(probe_rows)
-    n_rows = int(min(1 << 20, max(probe_rows, probe_rows * target_s / max(t, 1e-3))))
+    probe = min(256, BH * w.N)
+    t, f = run(probe)
+    n_rows = int(min(BH * w.N, max(probe, probe * target_s / max(t, 1e-4))))
     t, f = run(n_rows)
-    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
-            "kind": "oracle",
-            "sample": f"{n_rows} random query rows of {w.name} ({'causal' if causal else 'non-causal'}),"
-                      f" explicit fp64 attention per row, {t:.1f} s, {f / 1e9:.1f} GFLOP"}
+    return {"tflops": f / t / 1e12, "rows": n_rows, "seconds": round(t, 2),
+            "gflop": round(f / 1e9, 2)}
+
+
+def cpu_baseline(cases, headline, gpu_tflops, target_s=2.5):
+    """The fp64 oracle timed on the host cores on a bounded sample of every
+    benchmarked workload and mask, next to the GPU's rate on the same case.
+    The headline case is the reported value."""
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    rng = np.random.default_rng(123)
+    per = {}
+    for name, causal in cases:
+        key = f"{name}_{'causal' if causal else 'noncausal'}"
+        r = cpu_baseline_one(fa_inputs.WORKLOADS[name], causal, target_s, rng)
+        if key in gpu_tflops:
+            r["gpu_tflops"] = round(gpu_tflops[key], 2)
+            r["gpu_over_oracle"] = round(gpu_tflops[key] / r["tflops"], 1)
+        r["tflops"] = round(r["tflops"], 5)
+        per[key] = r
+        print(f"[bench] cpu oracle {key}: {r['tflops'] * 1e3:.2f} GFLOP/s "
+              f"({r['rows']} rows, {r['seconds']} s)", file=sys.stderr, flush=True)
+    head = per[headline]
+    return {"value": head["tflops"], "unit": "TFLOP/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{head['rows']} random query rows of {headline}, explicit fp64 attention "
+                      f"per row (the oracle as it stands, C + OpenMP), {head['seconds']} s, "
+                      f"{head['gflop']} GFLOP; every other benchmarked workload and mask sampled "
+                      f"the same way in per_workload",
+            "per_workload": per}
+
+
+def run_each_kernel_once(torch, fa, reps):
+    """Run every benchmarked kernel `reps` times with nothing else in between
+    (no timing, no clock sampling), for hardware-counter collection: the
+    forward on every workload and mask, split-KV (split and combine kernels)
+    on the two small grids, and the backward (dQ and dK/dV kernels) at the
+    headline shape, both masks."""
+    for name, w in fa_inputs.WORKLOADS.items():
+        (q, k, v), _ = _device_inputs(w, torch)
+        for causal in w.masks:
+            o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=w.scale)
+            for _ in range(reps):
+                fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale)
+            torch.cuda.synchronize()
+            print(f"[counters] forward {name} causal={causal}", file=sys.stderr, flush=True)
+    for small in SMALL_GRIDS:
+        (q, k, v), _ = _device_inputs(small, torch)
+        need = fa.fa_fwd_splitkv_workspace_size(small.B, small.H, small.N, small.N, small.D, 4)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        o, lse = torch.empty_like(q), torch.empty((small.B, small.H, small.N), device=q.device)
+        for _ in range(reps):
+            fa.fa_fwd_splitkv(q, k, v, o, lse, causal=False, scale=small.scale, num_splits=4,
+                              workspace=ws)
+        torch.cuda.synchronize()
+        print(f"[counters] split-KV {small.name} (4 splits)", file=sys.stderr, flush=True)
+    w = fa_inputs.WORKLOADS[fa_inputs.HEADLINE]
+    (q, k, v), _ = _device_inputs(w, torch)
+    dout = torch.randn(q.shape, device=q.device).to(q.dtype)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+        for _ in range(reps):
+            fa.fa_bwd(q, k, v, o, dout, lse, causal=causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                      delta=delta)
+        torch.cuda.synchronize()
+        print(f"[counters] backward {w.name} causal={causal}", file=sys.stderr, flush=True)
+
+
+# the small grids of the split-KV lines: the [B=8, N=1024, D=64] workload (64
+# workgroups of 128 query rows) and a [B=1, H=8, N=2048, D=128] one (128)
+SMALL_GRIDS = (fa_inputs.WORKLOADS["b8h1_n1024_d64_bf16"],
+               fa_inputs.Workload("b1h8_n2048_d128_bf16", 1, 8, 2048, 128, "bf16", 7, (False,)))
 
 
 def main():
@@ -324,6 +454,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="back-to-back untimed calls for at least this long before every timed "
+                         "line, on top of --warmup (default 1 s)")
     ap.add_argument("--workload", default=fa_inputs.HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -331,6 +464,9 @@ def main():
                     help="skip the 3 s clock reading under sustained load")
     ap.add_argument("--sweep-variants", action="store_true",
                     help="time every kernel variant on the N=4096 workloads and exit")
+    ap.add_argument("--counters-run", type=int, default=0, metavar="REPS",
+                    help="only run every benchmarked kernel REPS times (for hardware counters), "
+                         "then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) to calibrate "
                          "HBM byte counters, then exit")
@@ -360,6 +496,10 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if a.counters_run:
+        run_each_kernel_once(torch, fa, a.counters_run)
+        return
+
     w = fa_inputs.WORKLOADS[a.workload]
     if a.sweep_variants:
         for name in (w.name, "b4h16_n4096_d64_bf16", "b1h32_n16384_d128_bf16_q8"):
@@ -367,7 +507,8 @@ def main():
             for causal in wl.masks:
                 for var in range(fa.fa_num_variants()):
                     try:
-                        r = time_gpu(wl, causal, a.steps, a.warmup, torch, fa, variant=var)
+                        r = time_gpu(wl, causal, a.steps, a.warmup, torch, fa, variant=var,
+                                     settle_s=a.settle)
                     except fa.FAError as e:
                         print(f"[sweep] {name} causal={causal} {fa.fa_variant_name(var)}: {e}",
                               flush=True)
@@ -375,9 +516,16 @@ def main():
                     print(f"[sweep] {name} causal={int(causal)} {fa.fa_variant_name(var):28s} "
                           f"{r['ms']:.4f} ms {r['tflops']:7.1f} TFLOP/s", flush=True)
         return
-    head = time_gpu(w, False, a.steps, a.warmup, torch, fa)
-    print(f"[bench] {w.name} non-causal: {head['ms']:.4f} ms/step {head['tflops']:.1f} TFLOP/s",
+    head = time_gpu(w, False, a.steps, a.warmup, torch, fa, settle_s=a.settle)
+    print(f"[bench] {w.name} non-causal: {head['ms']:.4f} ms/step {head['tflops']:.1f} TFLOP/s "
+          f"(after {head['settle_s']} s / {head['settle_calls']} settle calls)",
           file=sys.stderr, flush=True)
+    head_key = f"{w.name}_noncausal"
+    gpu_rates = {head_key: head["tflops"]}
+    timing = {"headline": "mean of the timed back-to-back calls",
+              "warmup_calls": a.warmup, "settle_s": head["settle_s"],
+              "settle_calls": head["settle_calls"], "settle_last_ms": head["settle_last_ms"],
+              "timed_calls": a.steps, "timed_wall_s": round(head["wall_s"], 4)}
 
     extra = {}
     if not a.no_extra:
@@ -385,24 +533,24 @@ def main():
                              ("b4h16_n4096_d64_bf16", True), ("b2h16_n4000_d128_fp16", False),
                              ("b2h16_n4000_d128_fp16", True), ("b1h32_n16384_d128_bf16_q8", True)):
             r = time_gpu(fa_inputs.WORKLOADS[name], causal, max(10, a.steps // 2),
-                         max(5, a.warmup // 2), torch, fa)
+                         max(5, a.warmup // 2), torch, fa, settle_s=a.settle)
             key = f"{name}_{'causal' if causal else 'noncausal'}"
+            gpu_rates[key] = r["tflops"]
             extra[key] = {"ms": round(r["ms"], 5), "tflops": round(r["tflops"], 2),
-                          "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
+                          "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                          "settle_s": r["settle_s"]}
             print(f"[bench] {key}: {r['ms']:.4f} ms {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
                   flush=True)
-        # small grids: the [B=8, N=1024, D=64] workload (64 workgroups of 128
-        # query rows) and a [B=1, H=8, N=2048, D=128] one (128 workgroups),
-        # single pass against split-KV with the library's split choice
-        smalls = (fa_inputs.WORKLOADS["b8h1_n1024_d64_bf16"],
-                  fa_inputs.Workload("b1h8_n2048_d128_bf16", 1, 8, 2048, 128, "bf16", 7, (False,)))
-        for small in smalls:
+        # small grids, single pass against split-KV with the library's split choice
+        for small in SMALL_GRIDS:
             for causal in small.masks:
                 for split in (False, True):
                     r = time_gpu(small, causal, max(20, a.steps), max(10, a.warmup), torch, fa,
-                                 splitkv=split)
+                                 splitkv=split, settle_s=a.settle)
                     key = (f"{small.name}_{'causal' if causal else 'noncausal'}"
                            f"_{'splitkv' if split else 'single_pass'}")
+                    if not split:
+                        gpu_rates[f"{small.name}_{'causal' if causal else 'noncausal'}"] = r["tflops"]
                     extra[key] = {"ms": round(r["ms"], 5), "tflops": round(r["tflops"], 2),
                                   "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}
                     if split:
@@ -414,17 +562,21 @@ def main():
         # per-launch distribution of the headline call, back to back and with
         # the caches scrubbed before each call (512 MiB written, untimed)
         for scrub in (0, 512):
-            r = time_per_launch(w, False, max(20, a.steps), torch, fa, scrub_mib=scrub)
+            r = time_per_launch(w, False, max(20, a.steps), torch, fa, scrub_mib=scrub,
+                                settle_s=a.settle)
             r["tflops_at_median"] = round(head["flops"] / (r["median_ms"] * 1e-3) / 1e12, 2)
             key = f"{w.name}_noncausal_per_launch{'_scrubbed' if scrub else ''}"
             extra[key] = r
+            timing["per_launch_scrubbed_median_ms" if scrub else "per_launch_median_ms"] = \
+                r["median_ms"]
             print(f"[bench] {key}: median {r['median_ms']:.4f} ms (p10 {r['p10_ms']:.4f}, "
                   f"p90 {r['p90_ms']:.4f})", file=sys.stderr, flush=True)
 
         # the backward at the headline shape (fa_bwd: dQ kernel then dK/dV
         # kernel), FLOPs counted as 2.5x the forward's (five N x N x D products)
         for causal in (False, True):
-            r = time_bwd(w, causal, max(10, a.steps // 2), max(5, a.warmup // 2), torch, fa)
+            r = time_bwd(w, causal, max(10, a.steps // 2), max(5, a.warmup // 2), torch, fa,
+                         settle_s=a.settle)
             key = f"{w.name}_{'causal' if causal else 'noncausal'}_backward"
             extra[key] = {"ms": round(r["ms"], 5), "tflops": round(r["tflops"], 2),
                           "frac_of_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -456,9 +608,15 @@ def main():
             head["tflops"] / (PEAK_BF16_TFLOPS * clock_summary["sclk_mhz_median"] / 2400.0), 4)
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(w, False)
-        print(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads",
-              file=sys.stderr, flush=True)
+        cases = [(w.name, False)]
+        if not a.no_extra:
+            cases += [(w.name, True), ("b4h16_n4096_d64_bf16", False),
+                      ("b4h16_n4096_d64_bf16", True), ("b2h16_n4000_d128_fp16", False),
+                      ("b2h16_n4000_d128_fp16", True), ("b1h32_n16384_d128_bf16_q8", True),
+                      ("b8h1_n1024_d64_bf16", False), ("b8h1_n1024_d64_bf16", True)]
+        cpu = cpu_baseline(cases, head_key, gpu_rates, target_s=10.0 if a.no_extra else 2.5)
+        print(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads "
+              f"({cpu['cpu_model']})", file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC,
@@ -478,6 +636,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "timing": timing,
         "clock": clock_summary,
         "extra": extra,
     }
