@@ -23,11 +23,11 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
-enum Family { kDefault = -1, kSimple = 0, kPingPong = 1 };
+enum Family { kDefault = -1, kSimple = 0 };
 
 struct Variant {
   const char *name;
-  int family;      // kernel family; 16-bit inputs only for kPingPong
+  int family;      // kernel family
   int waves;       // waves per workgroup of the simple family (0 = per-shape default)
   int xcd_remap;
 };
@@ -37,8 +37,6 @@ const Variant kVariants[] = {
     {"default", kDefault, 0, 1},
     {"simple_bm128_xcd", kSimple, 4, 1},
     {"simple_bm128_linear", kSimple, 4, 0},
-    {"pingpong_bm256_xcd", kPingPong, 0, 1},
-    {"pingpong_bm256_linear", kPingPong, 0, 0},
     {"simple_bm256_xcd", kSimple, 8, 1},
     {"simple_bm256_linear", kSimple, 8, 0},
 };
@@ -63,7 +61,6 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
              : dtype == FA_DTYPE_FP16 ? fa_simple_instance_fp16((int)D, causal != 0, waves)
                                       : fa_simple_instance_bf16((int)D, causal != 0, waves);
       break;
-    case kPingPong: *out = fa_pingpong_instance(dtype, (int)D, causal != 0); break;
     default: return false;
   }
   return out->fn != nullptr;

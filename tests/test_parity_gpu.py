@@ -77,8 +77,8 @@ def test_key_length_mask(dtype, causal, n_kv):
         assert (o == 0).all() and np.isneginf(lse).all()
 
 
-VARIANTS = ["default", "simple_bm128_xcd", "simple_bm128_linear", "pingpong_bm256_xcd",
-            "pingpong_bm256_linear", "simple_bm256_xcd", "simple_bm256_linear"]
+VARIANTS = ["default", "simple_bm128_xcd", "simple_bm128_linear", "simple_bm256_xcd",
+            "simple_bm256_linear"]
 
 
 def test_variant_list():
