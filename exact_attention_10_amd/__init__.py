@@ -12,6 +12,8 @@ The functions mirror the C ABI of ``include/fa.h``:
   top-left or bottom-right causal mask;
 * :func:`fa_fwd_splitkv` -- the same result for small grids, with the keys
   of every query tile split over several workgroups and combined;
+* :func:`fa_fwd_splitkv_noalloc` -- the same split-KV computation with its
+  partials in the library's static scratch array (no allocation);
 * :func:`fa_bwd` -- the backward pass: dQ, dK, dV from the forward's inputs,
   output and log-sum-exp;
 * :func:`fa_fwd_nk` -- the same with only the first ``n_kv`` keys visible;
@@ -34,6 +36,9 @@ FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_CAUSAL_TOP_LEFT, FA_CAUSAL_BOTTOM_RIGHT = 0, 1
 _ALIGN = {"top-left": FA_CAUSAL_TOP_LEFT, "bottom-right": FA_CAUSAL_BOTTOM_RIGHT}
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGNMENT, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_ERR_SCRATCH = -5
+# bytes of the static device array behind fa_fwd_splitkv_noalloc (include/fa.h)
+FA_SPLITKV_SCRATCH_BYTES = 32 << 20
 
 # names and argument types of every exported symbol of include/fa.h
 _P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -42,6 +47,8 @@ SIGNATURES = {
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _I,
                             _P, ctypes.c_size_t, _P]),
+    "fa_fwd_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _F,
+                                    _I, _I, _P]),
     "fa_bwd": (_I, [_P] * 10 + [_I64] * 5 + [_I, _I, _F, _I, _P]),
     "fa_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I]),
     "fa_splitkv_auto_splits": (_I, [_I64, _I64, _I64, _I64, _I64]),
@@ -234,6 +241,29 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, *, causal=False, causal_align="top
                             B, H, Nq, Nk, D, int(bool(causal)), _ALIGN[causal_align],
                             float(scale), _dtype_code(q), int(num_splits), ws_ptr, ws_bytes,
                             _stream_handle(q, stream))
+    _check(rc)
+    return o, lse
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o=None, lse=None, *, causal=False, causal_align="top-left",
+                           scale=None, num_splits=0, stream=None, with_lse=True):
+    """Split-KV attention whose partials live in the library's static scratch
+    array (nothing is allocated by the library; see include/fa.h for the limit
+    and for why calls on one GPU must not overlap); returns (o, lse). Pass
+    ``o`` and ``lse`` to keep this wrapper from allocating them either."""
+    lib = load_library()
+    if causal_align not in _ALIGN:
+        raise ValueError(f"causal_align must be one of {sorted(_ALIGN)}")
+    o, lse = _prepare(q, k, v, o, lse, with_lse, same_length=False)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None,
+                                    B, H, Nq, Nk, D, int(bool(causal)), _ALIGN[causal_align],
+                                    float(scale), _dtype_code(q), int(num_splits),
+                                    _stream_handle(q, stream))
     _check(rc)
     return o, lse
 

@@ -3,8 +3,9 @@
 //
 // Every argument is validated before the first HIP call, so the library can
 // be loaded and its error paths exercised on a machine without a GPU. The
-// library allocates no memory and keeps no state; a launch is asynchronous on
-// the caller's stream.
+// library allocates no memory and keeps no per-call state; a launch is
+// asynchronous on the caller's stream. The one piece of device memory it owns
+// is the static scratch array of the no-allocation split-KV entry point.
 #include "fa.h"
 #include "fa_bwd.hpp"
 #include "fa_combine.hpp"
@@ -270,6 +271,64 @@ int launch_splitkv(const void *q, const void *k, const void *v, void *o, float *
 }
 
 // ---------------------------------------------------------------------------
+// Split-KV without allocation: the fp32 partials go to a file-scope device
+// array instead of a caller workspace. Each GPU holds its own copy of the
+// array from the first use until the process ends; every call on one GPU
+// reuses it, so calls that overlap on one GPU (different streams, no
+// ordering) race on it. Nothing in it has to start at zero: every split
+// writes all of its partial rows, including splits that see no key.
+
+__device__ __attribute__((aligned(256))) char scratch[FA_SPLITKV_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current. In host code the name `scratch` only
+// stands for the array; kernels get this address.
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_error, sizeof(g_hip_error), "%s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  static std::mutex mu;
+  static void *ptr[kMaxDevices] = {nullptr};
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      std::snprintf(g_hip_error, sizeof(g_hip_error), "scratch lookup: %s",
+                    e != hipSuccess ? hipGetErrorString(e) : "null address");
+      return FA_ERR_HIP;
+    }
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return FA_OK;
+}
+
+int launch_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                           int causal_align, float scale, int dtype, int num_splits,
+                           void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, Nq, Nk, Nk, D, causal_align, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (num_splits < 0 || num_splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
+  const int ns = num_splits ? num_splits : auto_splits(B, H, Nq, Nk, D);
+  if (ns == 1)   // single pass: no partials, nothing of the scratch is used
+    return launch(q, k, v, o, lse, B, H, Nq, Nk, Nk, D, causal, causal_align, scale, dtype, stream, 0);
+  if (split_layout(B, H, Nq, D, ns).bytes > (int64_t)FA_SPLITKV_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void *ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FA_OK) return rc;
+  return launch_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, causal, causal_align, scale, dtype, ns,
+                        ws, (size_t)FA_SPLITKV_SCRATCH_BYTES, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Backward: the dQ kernel (which also writes D = rowsum(dO * O)), then the
 // dK/dV kernel, on the caller's stream.
 
@@ -408,6 +467,14 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
                         num_splits, workspace, workspace_bytes, stream);
 }
 
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                           int causal_align, float scale, int dtype, int num_splits,
+                           void *stream) {
+  return launch_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, causal, causal_align, scale,
+                                dtype, num_splits, stream);
+}
+
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, void *dq, void *dk, void *dv, float *delta, int64_t B, int64_t H,
            int64_t Nq, int64_t Nk, int64_t D, int causal, int causal_align, float scale,
@@ -429,6 +496,7 @@ const char *fa_strerror(int code) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, variant or size";
     case FA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case FA_ERR_HIP: return g_hip_error;
+    case FA_ERR_SCRATCH: return "split-KV partials larger than the library's static scratch";
     default: return "unknown status code";
   }
 }

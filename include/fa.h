@@ -63,7 +63,8 @@ enum fa_status {
   FA_ERR_INVALID_ARG = -1, /* null pointer, size < 1, bad scale, overlap   */
   FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, unknown dtype, too large */
   FA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned              */
-  FA_ERR_HIP = -4          /* the HIP launch failed; see fa_strerror        */
+  FA_ERR_HIP = -4,         /* the HIP launch failed; see fa_strerror        */
+  FA_ERR_SCRATCH = -5      /* fa_fwd_splitkv_noalloc: partials too large    */
 };
 
 /*
@@ -124,6 +125,30 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
                    int64_t D, int causal, int causal_align, float scale,
                    int dtype, int num_splits, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * Split-KV forward that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation). The same computation and kernels as
+ * fa_fwd_splitkv, with the same arguments minus the workspace: the fp32
+ * partials live in a static device array inside the library,
+ * FA_SPLITKV_SCRATCH_BYTES bytes, one copy per GPU, held from the first use
+ * on that GPU until the process ends. Every call on one GPU reuses that
+ * array, so calls that may overlap on one GPU (different streams without
+ * ordering) race and must not be issued; calls ordered on one stream are
+ * fine. Its contents on entry do not matter. The first call on a GPU looks
+ * up the array's device address (no allocation).
+ * Errors: those of fa_fwd_splitkv for the shared arguments, and
+ * FA_ERR_SCRATCH, with nothing launched, when the partials for these sizes
+ * and num_splits, fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits)
+ * bytes, exceed FA_SPLITKV_SCRATCH_BYTES (every automatic split choice,
+ * num_splits = 0, fits).
+ */
+#define FA_SPLITKV_SCRATCH_BYTES (32u << 20)
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o,
+                           float *lse, int64_t B, int64_t H, int64_t Nq,
+                           int64_t Nk, int64_t D, int causal, int causal_align,
+                           float scale, int dtype, int num_splits, void *stream);
 
 /* Workspace bytes fa_fwd_splitkv needs for these sizes and num_splits (0 =
  * the library's choice); 0 when that is a single split, or for invalid sizes. */

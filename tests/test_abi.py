@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+    for n in ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
+              "fa_fwd_splitkv_workspace_size",
               "fa_splitkv_auto_splits", "fa_fwd_nk", "fa_fwd_variant", "fa_strerror", "fa_version",
               "fa_num_variants", "fa_variant_name"):
         assert n in names
@@ -174,6 +175,46 @@ def test_splitkv_auto_choice(lib):
 ])
 def test_splitkv_validation(lib, kw, code):
     assert call_split(lib, **kw) == code
+
+
+def call_split_noalloc(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=200, Nk=1000, D=64, causal=0,
+                       align=fa.FA_CAUSAL_TOP_LEFT, scale=0.125, dtype=fa.FA_DTYPE_BF16, ns=4):
+    return lib.fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, causal, align, scale,
+                                      dtype, ns, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ns=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(ns=33), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(align=5), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=Q), fa.FA_ERR_INVALID_ARG),
+    (dict(k=K + 8), fa.FA_ERR_ALIGNMENT),
+    # partials of 32 splits x 4096 query rows x 128 fp32 (64 MiB) exceed the
+    # 32 MiB scratch: refused before any HIP call
+    (dict(B=1, H=1, Nq=4096, Nk=1 << 16, D=128, ns=32), fa.FA_ERR_SCRATCH),
+])
+def test_splitkv_noalloc_validation(lib, kw, code):
+    assert call_split_noalloc(lib, **kw) == code
+    assert fa.fa_strerror(code)
+
+
+def test_splitkv_noalloc_scratch_covers_every_automatic_choice(lib):
+    """Every split count the library picks by itself (num_splits = 0) fits the
+    static scratch: grids of up to 128 query tiles are the only ones split."""
+    assert fa.FA_SPLITKV_SCRATCH_BYTES == 32 << 20
+    worst = 0
+    for D in (64, 128):
+        for BH in (1, 2, 3, 5, 8, 16, 31, 64, 100, 127, 128):
+            for nq in (1, 100, 128, 129, 1000, 4096, 16384):
+                for nk in (64, 1000, 4096, 1 << 16, 1 << 20):
+                    need = lib.fa_fwd_splitkv_workspace_size(1, BH, nq, nk, D, 0)
+                    worst = max(worst, need)
+                    assert need <= fa.FA_SPLITKV_SCRATCH_BYTES, (D, BH, nq, nk, need)
+    assert worst > (8 << 20)     # the sweep does reach sizable partials
 
 
 # fake addresses for the backward's extra tensors: [2,4,256,128] bf16 = 512 KiB each
