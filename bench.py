@@ -282,22 +282,25 @@ def measure_clock(w, torch, fa, seconds=3.0, settle_s=1.2):
 def time_per_launch(w, causal, reps, torch, fa, scrub_mib=0, settle_s=1.0):
     """Per-launch durations (median, p10, p90 in ms) from one event pair
     around each fa_fwd call; with scrub_mib > 0 each call is preceded by an
-    untimed write of that many MiB, so that K and V start outside the L2 and
-    the memory-side cache. The calls follow `settle_s` seconds of back-to-back
-    calls."""
+    untimed read of a buffer of that many MiB, so that Q, K and V start
+    outside the L2 and the memory-side cache. The sweep only reads (a sum into
+    a preallocated scalar): a write sweep would leave that many MiB of dirty
+    lines, whose write-back would then compete with the timed call for HBM.
+    The calls follow `settle_s` seconds of back-to-back calls."""
     (q, k, v), _ = _device_inputs(w, torch)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
-    scrub = (torch.empty(scrub_mib << 18, dtype=torch.float32, device=q.device)
+    scrub = (torch.ones(scrub_mib << 18, dtype=torch.float32, device=q.device)
              if scrub_mib else None)
+    scrub_out = torch.empty((), dtype=torch.float32, device=q.device)
     settle(lambda: fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream),
            stream, torch, settle_s)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
     for e0, e1 in events:
         if scrub is not None:
-            scrub.fill_(1.0)
+            torch.sum(scrub, dim=0, out=scrub_out)
         e0.record(stream)
         fa.fa_fwd(q, k, v, o, lse, causal=causal, scale=w.scale, stream=stream)
         e1.record(stream)
@@ -560,7 +563,7 @@ def main():
                           file=sys.stderr, flush=True)
 
         # per-launch distribution of the headline call, back to back and with
-        # the caches scrubbed before each call (512 MiB written, untimed)
+        # the caches scrubbed before each call (512 MiB read, untimed)
         for scrub in (0, 512):
             r = time_per_launch(w, False, max(20, a.steps), torch, fa, scrub_mib=scrub,
                                 settle_s=a.settle)
