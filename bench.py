@@ -56,11 +56,11 @@ def attention_bytes(B, H, N, D, esize, with_lse=True):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_kernel_bf16_d128_b4h16_n4096_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_twogroup_bf16_d128_b4h16_n4096_hbm_traffic.txt")
 
 
 # the sources that make up the headline forward kernel and its launch
-FORWARD_SOURCES = ("fa_kernel.hpp", "fa_inst_simple_bf16.hip", "fa_launch.hpp", "fa_api.hip", "fa.h")
+FORWARD_SOURCES = ("fa_kernel.hpp", "fa_kernel_pp.hpp", "fa_inst_pp.hip", "fa_launch.hpp", "fa_api.hip", "fa.h")
 
 
 def kernel_sources_digest():
@@ -602,7 +602,7 @@ def main():
         "traffic": stored_traffic(),
         "algorithmic_flops_per_launch": head["flops"],
         "algorithmic_bytes_per_launch": attention_bytes(w.B, w.H, w.N, w.D, esize),
-        "kernel": "fa_fwd_kernel<bf16, D=128, non-causal>",
+        "kernel": "fa_fwd_pp_kernel<bf16, D=128> (two-group schedule, non-causal)",
     }
     if clock_summary is not None:
         # the same fraction against the peak scaled to the clock the GPU ran at

@@ -24,7 +24,7 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
-enum Family { kDefault = -1, kSimple = 0 };
+enum Family { kDefault = -1, kSimple = 0, kTwoGroup = 1 };
 
 struct Variant {
   const char *name;
@@ -40,12 +40,19 @@ const Variant kVariants[] = {
     {"simple_bm128_linear", kSimple, 4, 0},
     {"simple_bm256_xcd", kSimple, 8, 1},
     {"simple_bm256_linear", kSimple, 8, 0},
+    {"twogroup_bm256_xcd", kTwoGroup, 8, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// The default is the simple family; 16-bit D=128 runs it with 8 waves (256
-// query rows share each K/V tile), which measured fastest there for both
-// masks (causal with paired query tiles), and every other shape with 4.
+// The default: 16-bit D=128 without a causal mask runs the two-group kernel
+// (bitwise the same result as the simple family, 1-3 % faster there); every
+// other case runs the simple family, 16-bit D=128 with 8 waves (256 query rows
+// share each K/V tile; fastest for the causal mask with paired query tiles)
+// and every other shape with 4. The two-group kernel is slower at D=64, whose
+// softmax outweighs its matrix work.
+bool default_is_twogroup(int dtype, int64_t D, int causal) {
+  return dtype != FA_DTYPE_FP32 && D == 128 && !causal;
+}
 int default_waves(int dtype, int64_t D, int causal) {
   (void)causal;
   return (dtype != FA_DTYPE_FP32 && D == 128) ? 8 : 4;
@@ -57,10 +64,18 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
   const int waves = var.waves ? var.waves : default_waves(dtype, D, causal);
   switch (var.family) {
     case kDefault:
+      if (default_is_twogroup(dtype, D, causal)) {
+        *out = fa_pp_instance(dtype, (int)D, false);
+        break;
+      }
+      [[fallthrough]];
     case kSimple:
       *out = dtype == FA_DTYPE_FP32   ? fa_simple_instance_fp32((int)D, causal != 0, waves)
              : dtype == FA_DTYPE_FP16 ? fa_simple_instance_fp16((int)D, causal != 0, waves)
                                       : fa_simple_instance_bf16((int)D, causal != 0, waves);
+      break;
+    case kTwoGroup:
+      *out = fa_pp_instance(dtype, (int)D, causal != 0);
       break;
     default: return false;
   }

@@ -78,7 +78,7 @@ def test_key_length_mask(dtype, causal, n_kv):
 
 
 VARIANTS = ["default", "simple_bm128_xcd", "simple_bm128_linear", "simple_bm256_xcd",
-            "simple_bm256_linear"]
+            "simple_bm256_linear", "twogroup_bm256_xcd"]
 
 
 def test_variant_list():
@@ -91,13 +91,16 @@ def test_variant_list():
 def test_variants(name, causal, dtype, D):
     """Every kernel variant (tile shape / schedule / workgroup order) computes
     the same attention; variants that only reorder workgroups agree bitwise.
-    The 8-wave schedules exist for 16-bit inputs only: fp32 is rejected."""
+    The 8-wave schedules exist for 16-bit inputs only: fp32 is rejected; the
+    two-group schedule has no causal mask either."""
     variant = VARIANTS.index(name)
     _banner(f"variant {variant} ({name}) dtype={dtype} D={D} causal={causal}")
     B, H, N = 2, 4, 520
     qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 500 + variant)
     scale = parity.default_scale(D)
-    if dtype == "fp32" and name != "default" and not name.startswith("simple_bm128"):
+    unsupported = (dtype == "fp32" and name != "default" and not name.startswith("simple_bm128")) \
+        or (name.startswith("twogroup") and causal)
+    if unsupported:
         with pytest.raises(fa.FAError):
             _run(qb, kb, vb, dtype, causal, scale, variant=variant)
         return
@@ -110,6 +113,29 @@ def test_variants(name, causal, dtype, D):
         if linear:
             o2, l2 = _run(qb, kb, vb, dtype, causal, scale, variant=linear[0])
             assert np.array_equal(o, o2) and np.array_equal(lse, l2), "workgroup order changed bits"
+
+
+TWOGROUP = VARIANTS.index("twogroup_bm256_xcd")
+
+
+@pytest.mark.parametrize("n_kv", [0, 1, 63, 64, 65, 128, 191, 192, 193, 255, 256, 257, 320,
+                                  449, 520])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64)])
+def test_twogroup_key_tails(dtype, D, n_kv):
+    """The two-group schedule streams 64-key tiles through four LDS stages
+    per matrix, loads K three tiles and V two tiles ahead, and unrolls its
+    loop by four periods: key counts from none to a ragged last tile, after
+    every remainder of tiles modulo 4, with a ragged query tail (520 = 2 * 256
+    + 8 rows), every element against the oracle."""
+    _banner(f"twogroup dtype={dtype} D={D} n_kv={n_kv}")
+    B, H, N = 1, 2, 520
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 900 + n_kv + D)
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, dtype, False, scale, n_kv=n_kv, variant=TWOGROUP)
+    o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, False, n_kv=n_kv)
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"twogroup n_kv={n_kv}")
+    if n_kv == 0:
+        assert (o == 0).all() and np.isneginf(lse).all()
 
 
 # ---------------------------------------------------------------------------
