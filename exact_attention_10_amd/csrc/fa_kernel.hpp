@@ -136,10 +136,17 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void *base, uint32_t byte
 }
 
 // Max over the two 32-lane halves: both halves end with the same value.
+// The larger of two scores. IEEE 754-2019 maximum (NaN-propagating) rather
+// than fmaxf (maxNum): the scores hold no NaN, so the two agree here, but
+// fmaxf must quiet each operand the compiler cannot prove canonical (MFMA
+// results, lane swaps) with an extra instruction, while gfx950 has
+// v_maximum3_f32, which needs none.
+__device__ __forceinline__ float score_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float halves_max(float x) {
   u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
       __float_as_uint(x), __float_as_uint(x), false, false));
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return score_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
@@ -477,11 +484,11 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     // section 3: rebasing multiplies every accumulated term by one common
     // factor), so this skips most accumulator rescales without changing the
     // result beyond rounding.
-    float mx = s[0][0];
+    float mx = score_max(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = score_max(mx, s[kb][i]);
     mx = halves_max(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, mx);

@@ -146,6 +146,8 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
 
   // ---- lane offsets of the operand fragments in stage 0 ----
   uint32_t k_off[NKC], v_off[2][NDB];
+  const FA_LDS char *k_ptr[NKC];
+  const FA_LDS char *v_ptr[2][NDB];
   {
     const int g = lane >> 4, r = (lane & 15) >> 2, cq = lane & 3;
 #pragma unroll
@@ -157,6 +159,23 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
         const int col = db * 32 + (g & 1) * 16 + cq * 4;
         const int key = jg * 8 + (g >> 1) * 4 + r;
         v_off[jg][db] = C::V_BASE + key * RB + ((((col * 2) / 16) ^ swz<RB>(key)) * 16) + (col * 2) % 16;
+      }
+    // LDS pointers formed once here. The empty asm hides the sum from the
+    // compiler, which would otherwise add the (zero) base of the dynamic LDS
+    // to each offset again inside the loop: eight adds per tile.
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      uint32_t a = smem_base + k_off[kc];
+      asm volatile("" : "+v"(a));
+      k_ptr[kc] = (const FA_LDS char *)(uintptr_t)a;
+    }
+#pragma unroll
+    for (int jg = 0; jg < 2; ++jg)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        uint32_t a = smem_base + v_off[jg][db];
+        asm volatile("" : "+v"(a));
+        v_ptr[jg][db] = (const FA_LDS char *)(uintptr_t)a;
       }
   }
 
@@ -192,12 +211,11 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
   // stage holds no tile yet; its reads are made but never used.) ----
   auto matrix = [&](int j, auto kst_c, auto vst_c) __attribute__((always_inline)) {
     constexpr int kst = decltype(kst_c)::value, vst = decltype(vst_c)::value;
-    const char *vl = smem + vst * C::TILE_BYTES;
     u32x4 vf[NPC][NDB];
     // transposing read r of chunk pc: head-dim block r / 2, half r % 2
     auto read_v1 = [&](int pc, int r) __attribute__((always_inline)) {
       const int db = r / 2, jg = r % 2;
-      const char *addr = vl + v_off[jg][db] + pc * 16 * RB;
+      const FA_LDS char *addr = v_ptr[jg][db] + vst * C::TILE_BYTES + pc * 16 * RB;
       const u32x2 xx = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)addr));
       vf[pc][db][jg * 2] = xx[0];
       vf[pc][db][jg * 2 + 1] = xx[1];
@@ -208,13 +226,12 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
     };
     __builtin_amdgcn_s_setprio(1);
     if (j < n) {
-      const char *kl = smem + kst * C::TILE_BYTES;
       constexpr int VR = 4 * NDB / (NKC / 2);        // V reads per S chunk, second half
       static_assert(VR * (NKC / 2) == 4 * NDB, "even spread of the V reads");
       u32x4 kf[NKC][2];
       auto read_k = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[kc][kb] = *(const FA_LDS u32x4 *)(kl + k_off[kc] + kb * 32 * RB);
+        for (int kb = 0; kb < 2; ++kb) kf[kc][kb] = *(const FA_LDS u32x4 *)(k_ptr[kc] + kst * C::TILE_BYTES + kb * 32 * RB);
       };
 #pragma unroll
       for (int kc = 0; kc < KW; ++kc) read_k(kc);
@@ -264,11 +281,11 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
           if (key >= n_kv) s[kb][i] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float mx = score_max(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = score_max(mx, s[kb][i]);
     mx = halves_max(mx) * c;
     // the reference moves only when a row max exceeds it by more than the
     // slack; acc and l are rescaled together ("A09", section 3, the rebasing)
@@ -285,8 +302,11 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
     // a row that has seen no visible key has only -inf scores: p = 0
     const float neg = (m_run == -INFINITY) ? 0.f : -m_run;
     float rs[4];
+    // per 32-key block: exponentials, row-sum terms, then its packed P^T
+    // chunks (chunk pc = keys pc*16 + 8*(w/2) + half*4 + ...: values
+    // (pc%2)*8 .. +7 of block pc/2)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, neg));
@@ -294,16 +314,16 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
         if (kb == 0 && i < 4) rs[i] = e;
         else rs[i % 4] += e;
       }
+#pragma unroll
+      for (int pc = 2 * kb; pc < 2 * kb + 2; ++pc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x = pack2<DT>(s[pc / 2][(pc % 2) * 8 + 2 * w], s[pc / 2][(pc % 2) * 8 + 2 * w + 1]);
+          pin(x);
+          pf[pc][w] = x;
+        }
+    }
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    // P^T chunk pc = keys pc*16 + 8*(w/2) + half*4 + ...: values (pc%2)*8 .. +7 of block pc/2
-#pragma unroll
-    for (int pc = 0; pc < NPC; ++pc)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t x = pack2<DT>(s[pc / 2][(pc % 2) * 8 + 2 * w], s[pc / 2][(pc % 2) * 8 + 2 * w + 1]);
-        pin(x);
-        pf[pc][w] = x;
-      }
   };
 
   // ---- end of period j: this group's transfer that period j+1 reads is
