@@ -346,6 +346,8 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   constexpr int NKO = (DT == DT_FP32) ? 1 : NKC;
   constexpr int NVO = (DT == DT_FP32) ? 1 : NDB;
   uint32_t k_off[NKO], v_off[2][NVO];
+  const FA_LDS char *k_ptr[NKO];
+  const FA_LDS char *v_ptr[2][NVO];
   if constexpr (DT != DT_FP32) {
     const int g = lane >> 4, r = (lane & 15) >> 2, cq = lane & 3;
 #pragma unroll
@@ -361,6 +363,23 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
         const int col = db * 32 + (g & 1) * 16 + cq * 4;
         const int key = jg * 8 + (g >> 1) * 4 + r;
         v_off[jg][db] = key * RB + ((((col * 2) / 16) ^ swz<RB>(key)) * 16) + (col * 2) % 16;
+      }
+    // LDS pointers formed once here. The empty asm hides the sum from the
+    // compiler, which would otherwise add the (zero) base of the dynamic LDS
+    // to each offset again inside the loop, once per fragment read group.
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      uint32_t a = smem_base + k_off[kc];
+      asm volatile("" : "+v"(a));
+      k_ptr[kc] = (const FA_LDS char *)(uintptr_t)a;
+    }
+#pragma unroll
+    for (int jg = 0; jg < 2; ++jg)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        uint32_t a = smem_base + v_off[jg][db];
+        asm volatile("" : "+v"(a));
+        v_ptr[jg][db] = (const FA_LDS char *)(uintptr_t)a;
       }
   }
 
@@ -422,7 +441,8 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
       u32x4 kf[NKC][NKB];
       auto read_k = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kf[kc][kb] = *(const FA_LDS u32x4 *)(kl + k_off[kc] + kb * 32 * RB);
+        for (int kb = 0; kb < NKB; ++kb)
+          kf[kc][kb] = *(const FA_LDS u32x4 *)(k_ptr[kc] + buf * (2 * C::TILE_BYTES) + kb * 32 * RB);
       };
 #pragma unroll
       for (int kc = 0; kc < KPIPE; ++kc) read_k(kc);
@@ -453,7 +473,7 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int jg = 0; jg < 2; ++jg) {
-            const char *addr = vl + v_off[jg][db] + pc * 16 * RB;
+            const FA_LDS char *addr = v_ptr[jg][db] + (buf * 2 + 1) * C::TILE_BYTES + pc * 16 * RB;
             const u32x2 xx = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4 *)addr));
             vf[pc][db][jg * 2] = xx[0];
             vf[pc][db][jg * 2 + 1] = xx[1];
