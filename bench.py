@@ -60,7 +60,8 @@ TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_twogroup_bf16_d128_b4h16_n4096_hbm
 
 
 # the sources that make up the headline forward kernel and its launch
-FORWARD_SOURCES = ("fa_kernel.hpp", "fa_kernel_pp.hpp", "fa_inst_pp.hip", "fa_launch.hpp", "fa_api.hip", "fa.h")
+FORWARD_SOURCES = ("fa_kernel.hpp", "fa_kernel_pp.hpp", "fa_kernel_pp16.hpp", "fa_inst_pp.hip", "fa_launch.hpp",
+                   "fa_api.hip", "fa.h")
 
 
 def kernel_sources_digest():
@@ -602,7 +603,7 @@ def main():
         "traffic": stored_traffic(),
         "algorithmic_flops_per_launch": head["flops"],
         "algorithmic_bytes_per_launch": attention_bytes(w.B, w.H, w.N, w.D, esize),
-        "kernel": "fa_fwd_pp_kernel<bf16, D=128> (two-group schedule, non-causal)",
+        "kernel": "fa_fwd_pp16_kernel<bf16, D=128> (two-group schedule on 16x16x32 MFMAs, non-causal)",
     }
     if clock_summary is not None:
         # the same fraction against the peak scaled to the clock the GPU ran at

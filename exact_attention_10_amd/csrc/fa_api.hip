@@ -24,7 +24,7 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
-enum Family { kDefault = -1, kSimple = 0, kTwoGroup = 1 };
+enum Family { kDefault = -1, kSimple = 0, kTwoGroup = 1, kTwoGroup16 = 2 };
 
 struct Variant {
   const char *name;
@@ -41,15 +41,17 @@ const Variant kVariants[] = {
     {"simple_bm256_xcd", kSimple, 8, 1},
     {"simple_bm256_linear", kSimple, 8, 0},
     {"twogroup_bm256_xcd", kTwoGroup, 8, 1},
+    {"twogroup16_bm256_xcd", kTwoGroup16, 8, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// The default: 16-bit D=128 without a causal mask runs the two-group kernel
-// (bitwise the same result as the simple family, 1-3 % faster there); every
+// The default: 16-bit D=128 without a causal mask runs the two-group kernel on
+// 16x16x32 MFMAs (3-5 % faster there than the same schedule on 32x32x16
+// MFMAs, which draw more power per FLOP at the board's power limit); every
 // other case runs the simple family, 16-bit D=128 with 8 waves (256 query rows
 // share each K/V tile; fastest for the causal mask with paired query tiles)
-// and every other shape with 4. The two-group kernel is slower at D=64, whose
-// softmax outweighs its matrix work.
+// and every other shape with 4. The two-group kernels are slower at D=64,
+// whose softmax outweighs its matrix work.
 bool default_is_twogroup(int dtype, int64_t D, int causal) {
   return dtype != FA_DTYPE_FP32 && D == 128 && !causal;
 }
@@ -65,7 +67,7 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
   switch (var.family) {
     case kDefault:
       if (default_is_twogroup(dtype, D, causal)) {
-        *out = fa_pp_instance(dtype, (int)D, false);
+        *out = fa_pp16_instance(dtype, (int)D, false);
         break;
       }
       [[fallthrough]];
@@ -76,6 +78,9 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
       break;
     case kTwoGroup:
       *out = fa_pp_instance(dtype, (int)D, causal != 0);
+      break;
+    case kTwoGroup16:
+      *out = fa_pp16_instance(dtype, (int)D, causal != 0);
       break;
     default: return false;
   }

@@ -1,25 +1,35 @@
-// Instances of the two-group forward kernel (fa_kernel_pp.hpp): 16-bit inputs,
-// D in {64, 128}, no causal mask.
-#include "fa_kernel_pp.hpp"
+// Instances of the two-group forward kernels (fa_kernel_pp.hpp on 32x32x16
+// MFMAs, fa_kernel_pp16.hpp on 16x16x32 MFMAs): 16-bit inputs, D in {64, 128},
+// no causal mask.
+#include "fa_kernel_pp16.hpp"
 #include "fa_launch.hpp"
 
 namespace {
-template <int DT, int D>
+template <int DT, int D, bool M16>
 FaLaunch make() {
   using C = fa::PPCfg<D>;
-  return {reinterpret_cast<const void *>(&fa::fa_fwd_pp_kernel<DT, D>), C::LDS_BYTES, C::BM, C::WAVES * 64, 0};
+  const void *fn = M16 ? reinterpret_cast<const void *>(&fa::fa_fwd_pp16_kernel<DT, D>)
+                       : reinterpret_cast<const void *>(&fa::fa_fwd_pp_kernel<DT, D>);
+  return {fn, C::LDS_BYTES, C::BM, C::WAVES * 64, 0};
 }
-template <int DT>
+template <int DT, bool M16>
 FaLaunch by_d(int d) {
-  if (d == 64) return make<DT, 64>();
-  if (d == 128) return make<DT, 128>();
+  if (d == 64) return make<DT, 64, M16>();
+  if (d == 128) return make<DT, 128, M16>();
   return {nullptr, 0, 0, 0};
 }
 }  // namespace
 
 FaLaunch fa_pp_instance(int dt, int d, bool causal) {
   if (causal) return {nullptr, 0, 0, 0};
-  if (dt == 1) return by_d<fa::DT_FP16>(d);
-  if (dt == 2) return by_d<fa::DT_BF16>(d);
+  if (dt == 1) return by_d<fa::DT_FP16, false>(d);
+  if (dt == 2) return by_d<fa::DT_BF16, false>(d);
+  return {nullptr, 0, 0, 0};
+}
+
+FaLaunch fa_pp16_instance(int dt, int d, bool causal) {
+  if (causal) return {nullptr, 0, 0, 0};
+  if (dt == 1) return by_d<fa::DT_FP16, true>(d);
+  if (dt == 2) return by_d<fa::DT_BF16, true>(d);
   return {nullptr, 0, 0, 0};
 }

@@ -389,6 +389,11 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY;     // exponent reference (base-2 units), same in both halves
   float l_run = 0.f;           // this lane's partial row sum (its half's keys)
+  // derived from m_run, updated only where it moves: the threshold past which
+  // a score moves the reference, and the exponent offset (0 for a row that
+  // has seen no visible key, whose scores are all -inf: p = 0)
+  float thr = -INFINITY;
+  float neg = 0.f;
   const float c = p.c;
 
   // one key tile; buf (0 or 1) is a compile-time constant so that every LDS
@@ -504,25 +509,28 @@ __global__ void __launch_bounds__(WAVES * 64, (DT == DT_FP32 ? 1 : 2)) fa_fwd_ke
     // section 3: rebasing multiplies every accumulated term by one common
     // factor), so this skips most accumulator rescales without changing the
     // result beyond rounding.
-    float mx = score_max(s[0][0], s[0][1]);
+    // A row max (scaled by c > 0, which keeps order) exceeds the threshold
+    // exactly when the maximum of one of its two lanes does, so the row max
+    // over both lanes is formed only when some row moves.
+    float lm = score_max(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = score_max(mx, s[kb][i]);
-    mx = halves_max(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) lm = score_max(lm, s[kb][i]);
+    if (__builtin_amdgcn_ballot_w64(lm * c > thr) != 0) {
+      const float mx = halves_max(lm) * c;
       const float m_new = fmaxf(m_run, mx);
       // alpha = 0 on the first visible tile (m_run = -inf), 1 if unchanged
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      thr = m_new + kRescaleSlack;
+      neg = (m_new == -INFINITY) ? 0.f : -m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     }
-    // a row that has seen no visible key has only -inf scores: p = 0
-    const float neg = (m_run == -INFINITY) ? 0.f : -m_run;
     // row sum in four interleaved partial sums (short dependency chains)
     float rs[4];
 #pragma unroll

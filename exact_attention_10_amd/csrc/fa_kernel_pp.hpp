@@ -196,6 +196,11 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY;     // exponent reference (base-2 units), same in both halves
   float l_run = 0.f;           // this lane's partial row sum
+  // derived from m_run, updated only where it moves: the threshold past which
+  // a score moves the reference, and the exponent offset (0 for a row that
+  // has seen no visible key, whose scores are all -inf: p = 0)
+  float thr = -INFINITY;
+  float neg = 0.f;
   const float c = p.c;
   f32x16 s[2];                 // S^T of the current tile: two 32-key blocks
   u32x4 pf[NPC];               // P^T of the last softmaxed tile, packed to 16 bits
@@ -281,26 +286,29 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp_kernel(Params p) {
           if (key >= n_kv) s[kb][i] = -INFINITY;
         }
     }
-    float mx = score_max(s[0][0], s[0][1]);
+    float lm = score_max(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = score_max(mx, s[kb][i]);
-    mx = halves_max(mx) * c;
-    // the reference moves only when a row max exceeds it by more than the
-    // slack; acc and l are rescaled together ("A09", section 3, the rebasing)
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) lm = score_max(lm, s[kb][i]);
+    // The reference moves only when a row max exceeds it by more than the
+    // slack; acc and l are rescaled together ("A09", section 3, the
+    // rebasing). A row max (scaled by c > 0, which keeps order) exceeds the
+    // threshold exactly when the maximum of one of its two lanes does, so the
+    // row max over both lanes is formed only when some row moves.
+    if (__builtin_amdgcn_ballot_w64(lm * c > thr) != 0) {
+      const float mx = halves_max(lm) * c;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      thr = m_new + kRescaleSlack;
+      neg = (m_new == -INFINITY) ? 0.f : -m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     }
-    // a row that has seen no visible key has only -inf scores: p = 0
-    const float neg = (m_run == -INFINITY) ? 0.f : -m_run;
     float rs[4];
     // per 32-key block: exponentials, row-sum terms, then its packed P^T
     // chunks (chunk pc = keys pc*16 + 8*(w/2) + half*4 + ...: values

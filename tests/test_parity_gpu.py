@@ -78,7 +78,7 @@ def test_key_length_mask(dtype, causal, n_kv):
 
 
 VARIANTS = ["default", "simple_bm128_xcd", "simple_bm128_linear", "simple_bm256_xcd",
-            "simple_bm256_linear", "twogroup_bm256_xcd"]
+            "simple_bm256_linear", "twogroup_bm256_xcd", "twogroup16_bm256_xcd"]
 
 
 def test_variant_list():
@@ -115,25 +115,23 @@ def test_variants(name, causal, dtype, D):
             assert np.array_equal(o, o2) and np.array_equal(lse, l2), "workgroup order changed bits"
 
 
-TWOGROUP = VARIANTS.index("twogroup_bm256_xcd")
-
-
 @pytest.mark.parametrize("n_kv", [0, 1, 63, 64, 65, 128, 191, 192, 193, 255, 256, 257, 320,
                                   449, 520])
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64)])
-def test_twogroup_key_tails(dtype, D, n_kv):
+@pytest.mark.parametrize("vname", ["twogroup_bm256_xcd", "twogroup16_bm256_xcd"])
+def test_twogroup_key_tails(vname, dtype, D, n_kv):
     """The two-group schedule streams 64-key tiles through four LDS stages
     per matrix, loads K three tiles and V two tiles ahead, and unrolls its
     loop by four periods: key counts from none to a ragged last tile, after
     every remainder of tiles modulo 4, with a ragged query tail (520 = 2 * 256
     + 8 rows), every element against the oracle."""
-    _banner(f"twogroup dtype={dtype} D={D} n_kv={n_kv}")
+    _banner(f"{vname} dtype={dtype} D={D} n_kv={n_kv}")
     B, H, N = 1, 2, 520
     qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 900 + n_kv + D)
     scale = parity.default_scale(D)
-    o, lse = _run(qb, kb, vb, dtype, False, scale, n_kv=n_kv, variant=TWOGROUP)
+    o, lse = _run(qb, kb, vb, dtype, False, scale, n_kv=n_kv, variant=VARIANTS.index(vname))
     o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, False, n_kv=n_kv)
-    parity.check(o, lse, o_ref, lse_ref, dtype, f"twogroup n_kv={n_kv}")
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"{vname} n_kv={n_kv}")
     if n_kv == 0:
         assert (o == 0).all() and np.isneginf(lse).all()
 
