@@ -24,7 +24,7 @@ constexpr int kVersion = 100;  // 0.1.0
 
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
-enum Family { kDefault = -1, kSimple = 0, kTwoGroup = 1, kTwoGroup16 = 2 };
+enum Family { kDefault = -1, kSimple = 0, kTwoGroup = 1, kTwoGroup16 = 2, kSimple16 = 3 };
 
 struct Variant {
   const char *name;
@@ -42,18 +42,23 @@ const Variant kVariants[] = {
     {"simple_bm256_linear", kSimple, 8, 0},
     {"twogroup_bm256_xcd", kTwoGroup, 8, 1},
     {"twogroup16_bm256_xcd", kTwoGroup16, 8, 1},
+    {"simple16_bm128_xcd", kSimple16, 4, 1},
+    {"simple16_bm256_xcd", kSimple16, 8, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// The default: 16-bit D=128 without a causal mask runs the two-group kernel on
+// The default. 16-bit D=128 without a causal mask runs the two-group kernel on
 // 16x16x32 MFMAs (3-5 % faster there than the same schedule on 32x32x16
-// MFMAs, which draw more power per FLOP at the board's power limit); every
-// other case runs the simple family, 16-bit D=128 with 8 waves (256 query rows
-// share each K/V tile; fastest for the causal mask with paired query tiles)
-// and every other shape with 4. The two-group kernels are slower at D=64,
-// whose softmax outweighs its matrix work.
-bool default_is_twogroup(int dtype, int64_t D, int causal) {
-  return dtype != FA_DTYPE_FP32 && D == 128 && !causal;
+// MFMAs, which draw more power per FLOP at the board's power limit). 16-bit
+// inputs with the causal mask run the simple schedule on 16x16x32 MFMAs (2-4 %
+// faster at D=128 and 1-2 % at D=64 than on 32x32x16; the two-group schedule
+// is slower there). 16-bit D=64 without the mask, whose softmax outweighs its
+// matrix work, and fp32 run the simple schedule on 32x32 MFMAs. 16-bit D=128
+// uses 8 waves (256 query rows share each K/V tile), every other shape 4.
+int default_family(int dtype, int64_t D, int causal) {
+  if (dtype == FA_DTYPE_FP32) return kSimple;
+  if (causal) return kSimple16;
+  return D == 128 ? kTwoGroup16 : kSimple;
 }
 int default_waves(int dtype, int64_t D, int causal) {
   (void)causal;
@@ -64,13 +69,8 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return false;
   if (D != 64 && D != 128) return false;
   const int waves = var.waves ? var.waves : default_waves(dtype, D, causal);
-  switch (var.family) {
-    case kDefault:
-      if (default_is_twogroup(dtype, D, causal)) {
-        *out = fa_pp16_instance(dtype, (int)D, false);
-        break;
-      }
-      [[fallthrough]];
+  const int family = var.family == kDefault ? default_family(dtype, D, causal) : var.family;
+  switch (family) {
     case kSimple:
       *out = dtype == FA_DTYPE_FP32   ? fa_simple_instance_fp32((int)D, causal != 0, waves)
              : dtype == FA_DTYPE_FP16 ? fa_simple_instance_fp16((int)D, causal != 0, waves)
@@ -81,6 +81,9 @@ bool pick(int dtype, int64_t D, int causal, const Variant &var, FaLaunch *out) {
       break;
     case kTwoGroup16:
       *out = fa_pp16_instance(dtype, (int)D, causal != 0);
+      break;
+    case kSimple16:
+      *out = fa_simple16_instance(dtype, (int)D, causal != 0, waves);
       break;
     default: return false;
   }

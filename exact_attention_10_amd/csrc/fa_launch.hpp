@@ -18,6 +18,8 @@ struct FaLaunch {
 FaLaunch fa_simple_instance_fp32(int d, bool causal, int waves);
 FaLaunch fa_simple_instance_fp16(int d, bool causal, int waves);
 FaLaunch fa_simple_instance_bf16(int d, bool causal, int waves);
+// the same schedule on 16x16x32 MFMAs (16-bit inputs only; null otherwise)
+FaLaunch fa_simple16_instance(int dt, int d, bool causal, int waves);
 // two-group forward (16-bit inputs, non-causal only; null otherwise)
 FaLaunch fa_pp_instance(int dt, int d, bool causal);
 // the same schedule on 16x16x32 MFMAs

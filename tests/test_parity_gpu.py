@@ -78,7 +78,8 @@ def test_key_length_mask(dtype, causal, n_kv):
 
 
 VARIANTS = ["default", "simple_bm128_xcd", "simple_bm128_linear", "simple_bm256_xcd",
-            "simple_bm256_linear", "twogroup_bm256_xcd", "twogroup16_bm256_xcd"]
+            "simple_bm256_linear", "twogroup_bm256_xcd", "twogroup16_bm256_xcd",
+            "simple16_bm128_xcd", "simple16_bm256_xcd"]
 
 
 def test_variant_list():
@@ -132,6 +133,26 @@ def test_twogroup_key_tails(vname, dtype, D, n_kv):
     o, lse = _run(qb, kb, vb, dtype, False, scale, n_kv=n_kv, variant=VARIANTS.index(vname))
     o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, False, n_kv=n_kv)
     parity.check(o, lse, o_ref, lse_ref, dtype, f"{vname} n_kv={n_kv}")
+    if n_kv == 0:
+        assert (o == 0).all() and np.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("n_kv", [0, 1, 31, 63, 65, 128, 160, 192, 257, 383, 449, 520])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("vname", ["simple16_bm128_xcd", "simple16_bm256_xcd"])
+def test_simple16_causal_key_tails(vname, dtype, D, n_kv):
+    """The causal 16x16x32 kernel splits its key loop at each wave's last
+    visible tile: full steps up to it, then steps that only keep the
+    workgroup's barriers and transfers going, starting on either LDS buffer.
+    Key counts that end before, on and past the diagonal of each query tile,
+    with a ragged query tail (520 rows), every element against the oracle."""
+    _banner(f"{vname} causal dtype={dtype} D={D} n_kv={n_kv}")
+    B, H, N = 1, 2, 520
+    qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 1900 + n_kv + D)
+    scale = parity.default_scale(D)
+    o, lse = _run(qb, kb, vb, dtype, True, scale, n_kv=n_kv, variant=VARIANTS.index(vname))
+    o_ref, lse_ref = parity.reference_full(qb, kb, vb, dtype, scale, True, n_kv=n_kv)
+    parity.check(o, lse, o_ref, lse_ref, dtype, f"{vname} causal n_kv={n_kv}")
     if n_kv == 0:
         assert (o == 0).all() and np.isneginf(lse).all()
 
