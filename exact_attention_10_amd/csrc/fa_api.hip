@@ -47,18 +47,18 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// The default. 16-bit D=128 without a causal mask runs the two-group kernel on
-// 16x16x32 MFMAs (3-5 % faster there than the same schedule on 32x32x16
-// MFMAs, which draw more power per FLOP at the board's power limit). 16-bit
-// inputs with the causal mask run the simple schedule on 16x16x32 MFMAs (2-4 %
-// faster at D=128 and 1-2 % at D=64 than on 32x32x16; the two-group schedule
-// is slower there). 16-bit D=64 without the mask, whose softmax outweighs its
-// matrix work, and fp32 run the simple schedule on 32x32 MFMAs. 16-bit D=128
-// uses 8 waves (256 query rows share each K/V tile), every other shape 4.
+// The default. 16-bit D=128 runs the two-group kernel on 16x16x32 MFMAs, with
+// or without the causal mask (3-5 % faster than the same schedule on 32x32x16
+// MFMAs, which draw more power per FLOP at the board's power limit; causal
+// 4-6 % faster than the simple schedule on 16x16x32). 16-bit D=64, whose
+// softmax outweighs its matrix work, runs the simple schedule: on 16x16x32
+// MFMAs with the causal mask (1-2 % faster there), on 32x32 ones without it.
+// fp32 runs the simple schedule on 32x32 MFMAs. 16-bit D=128 uses 8 waves
+// (256 query rows share each K/V tile), every other shape 4.
 int default_family(int dtype, int64_t D, int causal) {
   if (dtype == FA_DTYPE_FP32) return kSimple;
-  if (causal) return kSimple16;
-  return D == 128 ? kTwoGroup16 : kSimple;
+  if (D == 128) return kTwoGroup16;
+  return causal ? kSimple16 : kSimple;
 }
 int default_waves(int dtype, int64_t D, int causal) {
   (void)causal;

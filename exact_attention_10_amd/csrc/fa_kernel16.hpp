@@ -17,15 +17,6 @@
 
 namespace fa {
 
-// The lane index, formed by an mbcnt the compiler cannot merge with another:
-// used where a value derived from it would otherwise stay live across the key
-// loop, to be spilled to scratch and reloaded
-__device__ __forceinline__ int fresh_lane_id() {
-  int ln;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  return ln;
-}
-
 template <int DT, int D, bool CAUSAL, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64, 2) fa_fwd16_kernel(Params p) {
   static_assert(DT == DT_BF16 || DT == DT_FP16, "16-bit inputs only");

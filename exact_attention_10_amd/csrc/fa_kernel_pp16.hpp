@@ -1,5 +1,5 @@
 // Two-group FlashAttention-2 forward on 16x16x32 MFMAs (gfx950), 16-bit
-// inputs, no mask other than the end of the keys.
+// inputs, with or without the causal mask.
 //
 // The schedule is that of fa_kernel_pp.hpp (two groups of four waves, a
 // matrix phase M(j) = S(j) then PV(j-1) and a softmax phase X(j) per key
@@ -23,7 +23,15 @@
 //     V^T operand reads its keys in the same order.
 // The arithmetic per score is that of fa_kernel.hpp ("A09 - Advanced Triton &
 // FlashAttention", section 3, The kernel, in pseudocode); the row max and
-// the row sum take two lane swaps across the four lanes of a query.
+// the row sum take two lane swaps across the four lanes of a query. Under
+// the causal mask ("A09", section 3, causal tile skipping) the workgroup
+// streams the key tiles up to its last row's diagonal and every wave computes
+// all of them, masking element by element the tiles that reach past one of
+// its rows: a wave whose rows end earlier computes masked tiles rather than
+// idle, so the two waves of a SIMD keep equal work near the diagonal and the
+// overlap of one's matrix phase with the other's softmax holds there too.
+// Causal workgroups take a pair of query tiles (T-1-i, i) when the grid of
+// pairs still fills the chip, as fa_kernel.hpp does.
 #pragma once
 
 #include "fa_kernel_pp.hpp"
@@ -51,7 +59,17 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DT, int D>
+// The lane index, formed by an mbcnt the compiler cannot merge with another:
+// used where a value derived from it would otherwise stay live across the key
+// loop, to be spilled to scratch and reloaded (a reload waits for every
+// outstanding memory operation, the tile transfers included)
+__device__ __forceinline__ int fresh_lane_id() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
+}
+
+template <int DT, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   static_assert(DT == DT_BF16 || DT == DT_FP16, "16-bit inputs only");
   static_assert(D == 64 || D == 128, "head dim");
@@ -77,13 +95,28 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   const int i16 = lane & 15;
   const int g = lane >> 4;
 
+  // ---- which (head, query tile) this workgroup owns: as fa_kernel.hpp,
+  // with the causal grid's longest tiles first, or one workgroup per (head,
+  // pair of query tiles T-1-i and i), which then runs both in turn ----
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if (p.xcd_remap && (nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int bh = bid / p.nq_tiles;
-  const int qt = bid - bh * p.nq_tiles;
+  int bh = bid / p.nq_tiles;
+  int qt = bid - bh * p.nq_tiles;
+  if (CAUSAL) qt = p.nq_tiles - 1 - qt;
+  int second_qt = -1;
+  if (CAUSAL && p.pair) {
+    const int T = p.nq_tiles;
+    const int npairs = (T + 1) / 2;
+    int c = blockIdx.x;
+    if (p.xcd_remap && (nblk & 7) == 0) c = (c & 7) * (nblk >> 3) + (c >> 3);
+    bh = c / npairs;
+    const int pr = c - bh * npairs;
+    qt = T - 1 - pr;
+    second_qt = (pr != T - 1 - pr) ? pr : -1;
+  }
   const int64_t Nq = p.nq;
-  const int q_wave = qt * BM + wave * 32;          // the wave's first query row
+  const int coff = (int)p.coff;            // causal diagonal: key j visible when j <= i + coff
 
   const int64_t q_head = Nq * (int64_t)D;
   const int64_t k_head = p.nk * (int64_t)D;
@@ -91,30 +124,6 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   const char *kh = (const char *)p.k + (int64_t)bh * k_head * 2;
   const char *vh = (const char *)p.v + (int64_t)bh * k_head * 2;
   const int n_kv = (int)p.n_kv;
-  const int n = n_kv > 0 ? (n_kv + BN - 1) / BN : 0;     // key tiles
-
-  // ---- Q fragments (B operand of S^T = K Q^T): query block nb, head-dim
-  // chunk kc: row q_wave + 16 nb + i16, head dims 32 kc + 8 g .. +7. Inline
-  // asm like the transfers, so that the compiler counts neither and the
-  // explicit waits below are the only ones; rows at or past Nq lie beyond the
-  // buffer's range and read as zeros. ----
-  uint32_t qf[2][NKC][4];
-  {
-    const i32x4 qr = make_rsrc_words(qh, (uint32_t)(q_head * 2));
-    i32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(qr[i]);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const uint32_t off = (uint32_t)(q_wave + nb * 16 + i16) * RB + (uint32_t)((kc * 32 + g * 8) * 2);
-        u32x4 x;
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(x) : "v"(off), "s"(r) : "memory");
-#pragma unroll
-        for (int w = 0; w < 4; ++w) qf[nb][kc][w] = x[w];
-      }
-  }
 
   // ---- tile transfers, as in fa_kernel_pp.hpp ----
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
@@ -174,6 +183,43 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   // that computes it stays in this phase (the compiler would otherwise sink
   // the softmax past the barrier, next to the MFMAs that read P).
   auto pin = [](uint32_t &x) __attribute__((always_inline)) { asm volatile("" : "+v"(x)); };
+
+  for (int job = 0; job < 2; ++job) {
+  if (job == 1) {
+    if (second_qt < 0) break;
+    qt = second_qt;
+    pp_wait_vmcnt<0>();       // the first job's O stores are done: the counts below start from zero
+    __syncthreads();          // every wave is done with the first job's LDS stages
+  }
+  const int q0 = qt * BM;
+  const int q_wave = q0 + wave * 32;          // the wave's first query row
+  int kend = n_kv;
+  if (CAUSAL) kend = min(kend, q0 + BM + coff);
+  const int n = kend > 0 ? (kend + BN - 1) / BN : 0;     // key tiles of the workgroup
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query block nb, head-dim
+  // chunk kc: row q_wave + 16 nb + i16, head dims 32 kc + 8 g .. +7. Inline
+  // asm like the transfers, so that the compiler counts neither and the
+  // explicit waits below are the only ones; rows at or past Nq lie beyond the
+  // buffer's range and read as zeros. ----
+  uint32_t qf[2][NKC][4];
+  {
+    const int qln = fresh_lane_id();
+    const i32x4 qr = make_rsrc_words(qh, (uint32_t)(q_head * 2));
+    i32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(qr[i]);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const uint32_t off = (uint32_t)(q_wave + nb * 16 + (qln & 15)) * RB + (uint32_t)((kc * 32 + (qln >> 4) * 8) * 2);
+        u32x4 x;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(x) : "v"(off), "s"(r) : "memory");
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qf[nb][kc][w] = x[w];
+      }
+  }
 
   // ---- running state: per query block nb ----
   f32x4 acc[NDB][2];
@@ -263,14 +309,24 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   auto softmax = [&](int j) __attribute__((always_inline)) {
     if (j < 0 || j >= n) return;
     const int kstart = j * BN;
-    if (kstart + BN > n_kv) {
+    // masks only on the tile past the end of the keys and, under the causal
+    // mask, on tiles that reach past a row of the wave
+    if (kstart + BN > n_kv || (CAUSAL && kstart + BN - 1 > q_wave + coff)) {
+      const int ln = fresh_lane_id();
+      const int rel = kstart + ((ln >> 2) & ~3);
+      int lim[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        lim[nb] = n_kv - 1 - rel;
+        if (CAUSAL) lim[nb] = min(lim[nb], q_wave + coff + nb * 16 + (ln & 15) - rel);
+      }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kstart + mb * 16 + 4 * g + i;
-          if (key >= n_kv) s[mb][0][i] = s[mb][1][i] = -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            if (mb * 16 + i > lim[nb]) s[mb][nb][i] = -INFINITY;
     }
     // this lane's maximum of each row (a quarter of the row's keys)
     float lm[2];
@@ -383,26 +439,28 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   }
 
   // ---- finalize: O = acc / l, LSE = (m + log2 l) ln 2 ----
+  const int oln = fresh_lane_id();
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float l_tot = quad_sum(l_run[nb]);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const int64_t q = q_wave + nb * 16 + i16;
+    const int64_t q = q_wave + nb * 16 + (oln & 15);
     if (q < Nq) {
       char *orow = (char *)p.o + ((int64_t)bh * q_head + q * D) * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d0 = db * 16 + 4 * g;
+        const int d0 = db * 16 + 4 * (oln >> 4);
         const uint32_t w0 = pack2<DT>(acc[db][nb][0] * inv, acc[db][nb][1] * inv);
         const uint32_t w1 = pack2<DT>(acc[db][nb][2] * inv, acc[db][nb][3] * inv);
         *(u32x2 *)(orow + d0 * 2) = u32x2{w0, w1};
       }
-      if (p.lse && g == 0) {
+      if (p.lse && oln < 16) {
         const float lse = l_tot > 0.f ? (m_run[nb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
         p.lse[(int64_t)bh * Nq + q] = lse;
       }
     }
   }
+  }  // job
 }
 
 }  // namespace fa

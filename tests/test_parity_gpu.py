@@ -93,14 +93,14 @@ def test_variants(name, causal, dtype, D):
     """Every kernel variant (tile shape / schedule / workgroup order) computes
     the same attention; variants that only reorder workgroups agree bitwise.
     The 8-wave schedules exist for 16-bit inputs only: fp32 is rejected; the
-    two-group schedule has no causal mask either."""
+    two-group schedule on 32x32x16 MFMAs has no causal mask either."""
     variant = VARIANTS.index(name)
     _banner(f"variant {variant} ({name}) dtype={dtype} D={D} causal={causal}")
     B, H, N = 2, 4, 520
     qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 500 + variant)
     scale = parity.default_scale(D)
     unsupported = (dtype == "fp32" and name != "default" and not name.startswith("simple_bm128")) \
-        or (name.startswith("twogroup") and causal)
+        or (name == "twogroup_bm256_xcd" and causal)
     if unsupported:
         with pytest.raises(fa.FAError):
             _run(qb, kb, vb, dtype, causal, scale, variant=variant)
@@ -139,13 +139,16 @@ def test_twogroup_key_tails(vname, dtype, D, n_kv):
 
 @pytest.mark.parametrize("n_kv", [0, 1, 31, 63, 65, 128, 160, 192, 257, 383, 449, 520])
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64)])
-@pytest.mark.parametrize("vname", ["simple16_bm128_xcd", "simple16_bm256_xcd"])
-def test_simple16_causal_key_tails(vname, dtype, D, n_kv):
-    """The causal 16x16x32 kernel splits its key loop at each wave's last
-    visible tile: full steps up to it, then steps that only keep the
-    workgroup's barriers and transfers going, starting on either LDS buffer.
-    Key counts that end before, on and past the diagonal of each query tile,
-    with a ragged query tail (520 rows), every element against the oracle."""
+@pytest.mark.parametrize("vname", ["simple16_bm128_xcd", "simple16_bm256_xcd", "twogroup16_bm256_xcd"])
+def test_causal_16x16x32_key_tails(vname, dtype, D, n_kv):
+    """The causal kernels on 16x16x32 MFMAs. The simple schedule splits its
+    key loop at each wave's last visible tile: full steps up to it, then steps
+    that only keep the workgroup's barriers and transfers going, starting on
+    either LDS buffer. The two-group schedule has every wave compute every
+    tile of its workgroup, masked past the wave's rows, through its four-stage
+    rings. Key counts that end before, on and past the diagonal of each query
+    tile, with a ragged query tail (520 rows), every element against the
+    oracle."""
     _banner(f"{vname} causal dtype={dtype} D={D} n_kv={n_kv}")
     B, H, N = 1, 2, 520
     qb, kb, vb = fa_inputs.draw_qkv(B, H, N, D, dtype, 1900 + n_kv + D)
