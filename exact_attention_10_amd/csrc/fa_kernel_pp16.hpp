@@ -25,10 +25,11 @@
 // FlashAttention", section 3, The kernel, in pseudocode); the row max and
 // the row sum take two lane swaps across the four lanes of a query. Under
 // the causal mask ("A09", section 3, causal tile skipping) the workgroup
-// streams the key tiles up to its last row's diagonal and every wave computes
-// all of them, masking element by element the tiles that reach past one of
-// its rows: a wave whose rows end earlier computes masked tiles rather than
-// idle, so the two waves of a SIMD keep equal work near the diagonal and the
+// streams the key tiles up to its last row's diagonal and every wave runs
+// both phases on all of them, masking element by element the tiles that
+// reach past one of its rows. On a tile wholly past its rows a wave skips the
+// products and their LDS reads but still runs the (fully masked) softmax, so
+// the two waves of a SIMD keep their phases in step near the diagonal and the
 // overlap of one's matrix phase with the other's softmax holds there too.
 // Causal workgroups take a pair of query tiles (T-1-i, i) when the grid of
 // pairs still fills the chip, as fa_kernel.hpp does.
@@ -196,6 +197,10 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   int kend = n_kv;
   if (CAUSAL) kend = min(kend, q0 + BM + coff);
   const int n = kend > 0 ? (kend + BN - 1) / BN : 0;     // key tiles of the workgroup
+  // tiles [t_live, n) hold only keys past every row of this wave: their
+  // products and fragment reads are skipped; the softmax still runs on them,
+  // and its causal mask sets every score of such a tile to -inf
+  const int t_live = CAUSAL ? (q_wave + 31 + coff >= 0 ? (q_wave + 31 + coff) / BN + 1 : 0) : n;
 
   // ---- Q fragments (B operand of S^T = K Q^T): query block nb, head-dim
   // chunk kc: row q_wave + 16 nb + i16, head dims 32 kc + 8 g .. +7. Inline
@@ -258,7 +263,7 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
       }
     };
     __builtin_amdgcn_s_setprio(1);
-    if (j < n) {
+    if (j < n && j < t_live) {
       u32x4 kf[NKF];
       // K fragment f = kc * NMB + mb
       auto read_k = [&](int f) __attribute__((always_inline)) {
@@ -287,12 +292,12 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
+    } else if (j >= 1 && j - 1 < t_live) {
 #pragma unroll
       for (int f = 0; f < VW; ++f) read_v(f);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (j >= 1) {
+    if (j >= 1 && j - 1 < t_live) {
 #pragma unroll
       for (int f = 0; f < NVF; ++f) {
         const int pc = f / NDB, db = f % NDB;
