@@ -392,6 +392,29 @@ def test_paired_causal_cross_sampled(D, align):
             parity.check_grad(g, ref, "bf16", f"paired bwd {align} head ({b},{h}) {n}")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 128), ("bf16", 64)])
+def test_paired_causal_more_queries_than_keys(dtype, D):
+    """Bottom-right causal with Nq > Nk on a grid large enough to pair query
+    tiles: the diagonal offset Nk - Nq is negative, so the first Nq - Nk rows
+    see no key (O = 0, LSE = -inf) and whole query tiles, and whole waves of
+    the tiles that straddle that boundary, have nothing to compute. Every row
+    of two heads and sampled rows of the rest, O and LSE against the oracle."""
+    B, H, nq, nk = 8, 16, 2500, 1000
+    _banner(f"paired causal Nq > Nk dtype={dtype} D={D}")
+    qb, kb, vb = fa_inputs.draw_qkv_cross(B, H, nq, nk, D, dtype, 6160 + D)
+    scale = parity.default_scale(D)
+    o, lse = _run_ex(qb, kb, vb, dtype, True, "bottom-right", scale)
+    o = o.reshape(B * H, nq, D)
+    lse = lse.reshape(B * H, nq)
+    full = np.array([(bh, i) for bh in (0, B * H - 1) for i in range(nq)], dtype=np.int64)
+    rows = np.unique(np.concatenate([full, parity.sample_rows(B, H, nq, 300, seed=D)]), axis=0)
+    q, k, v = (fa_inputs.to_f32(x, dtype) for x in (qb, kb, vb))
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, True, rows, causal_align="bottom-right")
+    parity.check(o[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], o_ref, lse_ref, dtype,
+                 f"paired causal Nq > Nk {dtype} D={D}")
+    assert (o[:, : nq - nk] == 0).all() and np.isneginf(lse[:, : nq - nk]).all()
+
+
 # ---------------------------------------------------------------------------
 # Split-KV (fa_fwd_splitkv): the same attention, keys split over workgroups
 
