@@ -1,4 +1,4 @@
-// Instances of the default schedule on 16x16x32 MFMAs (fa_kernel16.hpp) for
+// Instances of the simple schedule on 16x16x32 MFMAs (fa_kernel16.hpp) for
 // 16-bit inputs: D in {64, 128}, both masks, 4 or 8 waves per workgroup.
 #include "fa_kernel16.hpp"
 #include "fa_launch.hpp"

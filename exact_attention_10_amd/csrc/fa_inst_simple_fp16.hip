@@ -1,4 +1,4 @@
-// Instances of the default kernel (fa_kernel.hpp) for fp16 inputs: D in {64, 128},
+// Instances of the simple-schedule kernel (fa_kernel.hpp) for fp16 inputs: D in {64, 128},
 // both masks, 4 or 8 waves per workgroup. One translation unit per dtype so the
 // instances compile in parallel.
 #include "fa_kernel.hpp"

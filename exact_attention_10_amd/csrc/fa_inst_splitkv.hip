@@ -1,4 +1,4 @@
-// Instances of the split-KV forward: the default kernel in split mode (4
+// Instances of the split-KV forward: the simple-schedule kernel in split mode (4
 // waves, fp32 partials) for every dtype, D in {64, 128} and both masks, and
 // the combine kernel.
 #include "fa_combine.hpp"
