@@ -238,8 +238,12 @@ __global__ void __launch_bounds__(512, 2) fa_fwd_pp16_kernel(Params p) {
   float thr[2] = {-INFINITY, -INFINITY};
   float neg[2] = {0.f, 0.f};
   const float c = p.c;
-  f32x4 s[NMB][2];             // S^T of the current tile
+  // S^T of the current tile (zero until a matrix phase writes it: the
+  // softmax of a tile whose products this wave skips reads it, all masked)
+  f32x4 s[NMB][2];
   u32x4 pf[NPC][2];            // P^T of the last softmaxed tile, packed to 16 bits
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) s[mb][0] = s[mb][1] = f32x4{};
 #pragma unroll
   for (int pc = 0; pc < NPC; ++pc) pf[pc][0] = pf[pc][1] = u32x4{0, 0, 0, 0};
 

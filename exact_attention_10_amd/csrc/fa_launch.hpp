@@ -22,9 +22,9 @@ FaLaunch fa_simple_instance_bf16(int d, bool causal, int waves);
 FaLaunch fa_simple16_instance(int dt, int d, bool causal, int waves);
 // two-group forward (16-bit inputs, non-causal only; null otherwise)
 FaLaunch fa_pp_instance(int dt, int d, bool causal);
-// the same schedule on 16x16x32 MFMAs
+// the same schedule on 16x16x32 MFMAs (16-bit inputs, both masks; null otherwise)
 FaLaunch fa_pp16_instance(int dt, int d, bool causal);
-// split-KV: the default kernel in split mode (4 waves) and the combine kernel
+// split-KV: the simple-schedule kernel in split mode (4 waves) and the combine kernel
 FaLaunch fa_splitkv_instance(int dt, int d, bool causal);
 const void *fa_combine_instance(int dt, int d);
 
